@@ -1,0 +1,132 @@
+"""Each test plants one plausible mistake in the oracle (on the CPU, through
+monkeypatch) and checks that at least one pin then fails. This shows the pins
+are sensitive to dropped terms, wrong signs, wrong indices and transposed
+operands, not only that the oracle passes them."""
+
+import numpy as np
+import pytest
+
+from oracle import qblk_oracle as o
+from tests import test_oracle_invariants as inv
+from tests import test_oracle_pins as pins
+
+
+def _round_half_even(v):
+    return np.round(np.asarray(v, np.float64))
+
+
+def test_mutant_round_half_even_is_caught(monkeypatch):
+    monkeypatch.setattr(o, "round_half_away", _round_half_even)
+    with pytest.raises(AssertionError):
+        pins.test_round_half_away_matches_decimal()
+
+
+def test_mutant_q4_0_divides_by_8_is_caught(monkeypatch):
+    monkeypatch.setattr(o, "quantize_q4_0", lambda w: o.quantize_symmetric(w, 8))
+    with pytest.raises(AssertionError):
+        pins.test_q4_0_example_symmetric_rule()
+
+
+def test_mutant_swapped_nibbles_is_caught(monkeypatch):
+    def swapped(codes):
+        c = np.asarray(codes, np.int64)
+        return (c[..., 1::2] | (c[..., 0::2] << 4)).astype(np.uint8)
+    monkeypatch.setattr(o, "_nibble_pairs", swapped)
+    with pytest.raises(AssertionError):
+        pins.test_q4_0_pack_matches_page_scalar_kernel()
+
+
+def test_mutant_missing_offset_8_is_caught(monkeypatch):
+    orig = o.pack_q4_0
+
+    def no_offset(q, d):
+        # stores the two's-complement low nibble instead of q + 8
+        return orig((np.asarray(q) & 15) - 8, d)
+    monkeypatch.setattr(o, "pack_q4_0", no_offset)
+    with pytest.raises(AssertionError):
+        pins.test_q4_0_pack_matches_page_scalar_kernel()
+
+
+def test_mutant_dropped_q4_k_min_term_is_caught(monkeypatch):
+    def no_min(enc, aq, da, sa):
+        scale, _ = o.q4_k_sub_scales(enc)
+        S = o.block_sums(enc["q"], aq).astype(np.float64)
+        y = np.einsum("mnb,nb,mb->mn", S, scale, np.asarray(da, np.float64))
+        return y.astype(np.float32), y
+    monkeypatch.setattr(o, "product_q4_k", no_min)
+    with pytest.raises(AssertionError):
+        inv.test_product_equals_dequantized_dot(o.TYPE_Q4_K)
+
+
+def test_mutant_wrong_dmin_sign_is_caught(monkeypatch):
+    orig = o.quantize_q4_k
+
+    def pos_dmin(w):
+        enc = orig(w)
+        enc["dmin_bits"] = enc["dmin_bits"] & 0x7FFF
+        return enc
+    monkeypatch.setattr(o, "quantize_q4_k", pos_dmin)
+    with pytest.raises(AssertionError):
+        inv.test_q4_k_round_trip_bound_and_ranges()
+
+
+def test_mutant_transposed_block_sums_is_caught(monkeypatch):
+    def transposed(wq, aq):
+        wq = np.asarray(wq, np.int64)
+        aq = np.asarray(aq, np.int64)
+        N, K = wq.shape
+        M = aq.shape[0]
+        nb = K // 32
+        r = np.einsum("mbi,nbi->nmb", aq.reshape(M, nb, 32), wq.reshape(N, nb, 32))
+        return r.reshape(M, N, nb)
+    monkeypatch.setattr(o, "block_sums", transposed)
+    with pytest.raises(AssertionError):
+        inv.test_block_sums_brute_force(o.TYPE_Q8_0, 3, 256, 5)
+
+
+def test_mutant_block_index_off_by_one_is_caught(monkeypatch):
+    orig = o.block_sums
+
+    def shifted(wq, aq):
+        return np.roll(orig(wq, aq), 1, axis=-1)
+    monkeypatch.setattr(o, "block_sums", shifted)
+    with pytest.raises(AssertionError):
+        inv.test_product_equals_dequantized_dot(o.TYPE_Q4_0)
+
+
+def test_mutant_sub_scale_index_is_caught(monkeypatch):
+    orig = o.q4_k_sub_scales
+
+    def rolled(enc):
+        s, m = orig(enc)
+        return np.roll(s, 1, axis=-1), m
+    monkeypatch.setattr(o, "q4_k_sub_scales", rolled)
+    with pytest.raises(AssertionError):
+        inv.test_q4_k_hand_built_block_dequant()
+
+
+def test_mutant_fp16_nearest_instead_of_ceiling_is_caught(monkeypatch):
+    def nearest(v, c):
+        h = (np.asarray(v, np.float64) / c).astype(np.float16)
+        return h.view(np.uint16).astype(np.int64)
+    monkeypatch.setattr(o, "f16_ceil_div", nearest)
+    with pytest.raises(AssertionError):
+        pins.test_f16_ceil_div_brute_force()
+
+
+def test_mutant_activation_sum_of_abs_is_caught(monkeypatch):
+    orig = o.quantize_act
+
+    def abs_sum(x):
+        q, d, s = orig(x)
+        M, K = q.shape
+        return q, d, np.abs(q).reshape(M, K // 32, 32).sum(-1)
+    monkeypatch.setattr(o, "quantize_act", abs_sum)
+    with pytest.raises(AssertionError):
+        inv.test_block_sums_brute_force(o.TYPE_Q4_K, 2, 512, 2)
+
+
+def test_mutant_group8_order_is_caught(monkeypatch):
+    monkeypatch.setattr(o, "GROUP8_ORDER", np.array([0, 1, 2, 3, 4, 5, 6, 7]))
+    with pytest.raises(AssertionError):
+        inv.test_activation_buffer_layout()

@@ -1,0 +1,158 @@
+"""Pins of the oracle against what the pages print and against library
+routines / brute force. CPU only."""
+
+import json
+import os
+from decimal import Decimal, ROUND_HALF_UP
+
+import numpy as np
+import pytest
+
+from oracle import qblk_oracle as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- worked examples
+
+def test_worked_example_block_scale_0_08():
+    """tech-blog page, 量化是怎么做到的？: round(x / 0.08) and codes * 0.08."""
+    g = _golden("p4_worked_example.json")
+    x = np.array(g["weights"], dtype=np.float32)
+    s = np.float32(g["scale"])
+    codes = o.round_half_away((x / s).astype(np.float64))
+    assert codes.tolist() == g["codes"]
+    q = np.zeros(32, dtype=np.int64)
+    q[:4] = g["codes"]
+    rec = o.dequant_symmetric(q[None, :], np.array([[s]], np.float32))[0, :4]
+    assert np.allclose(rec, g["reconstructed"], rtol=0, atol=1e-7)
+
+
+def test_q4_0_example_symmetric_rule():
+    """runguoli page §5.1 example: scale 0.5, Q = [1,-2,2,7,-1]."""
+    g = _golden("p2_q4_0_example.json")
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :5] = g["weights"]
+    q, d = o.quantize_q4_0(x)
+    assert float(d[0, 0]) == g["scale"]
+    assert q[0, :5].tolist() == g["codes"]
+    assert np.all(q[0, 5:] == 0)
+    rec = o.dequant_symmetric(q, d)[0, :5]
+    assert rec.tolist() == g["reconstructed"]
+    err = np.abs(x[0, :5].astype(np.float64) - rec)
+    assert np.allclose(err, g["error_magnitudes"], rtol=0, atol=1e-6)
+
+
+def test_bits_per_weight_closed_forms():
+    """runguoli page §5.3-§5.5 field lists; totals recomputed with the
+    library's field widths (fp32 Q4_0 scale, 6-bit Q4_K codes)."""
+    g = _golden("p2_bits_per_weight.json")
+    for key in ("q4_0", "q8_0", "q4_k"):
+        e = g[key]
+        assert sum(e["fields"].values()) == e["total_bits"]
+        assert e["total_bits"] / e["block"] == e["bpw"]
+    K = 4096
+    q40 = dict(g["q4_0"]["fields"], scale=32)
+    assert o.row_bytes(o.TYPE_Q4_0, K) * 8 == sum(q40.values()) * K // 32
+    assert o.row_bytes(o.TYPE_Q8_0, K) * 8 == g["q8_0"]["total_bits"] * K // 32
+    q4k = dict(g["q4_k"]["fields"], scales=48, mins=48)
+    assert o.row_bytes(o.TYPE_Q4_K, K) * 8 == sum(q4k.values()) * K // 256
+    assert o.row_bytes(o.TYPE_Q4_K, K) / K * 8 == 4.5
+    # activation buffer: 8-bit codes + fp32 scale + int32 sum per 32
+    assert o.act_bytes(3, K) * 8 == 3 * K * (8 + 64 / 32)
+
+
+# ---------------------------------------------------------------- scalar kernel of §6.4
+
+def _page_q4_0_float_dot(packed_row, K, yf):
+    """The scalar Q4_0 dot of runguoli page §6.4, restated: for every block,
+    take its scale; for every byte j of the block, low nibble - 8 pairs with
+    float activation 2j and high nibble - 8 with 2j+1; accumulate
+    (code * scale) * activation. Reads the library's row layout."""
+    nb = K // 32
+    scales = packed_row[:4 * nb].copy().view("<f4")
+    qs = packed_row[o.header_bytes(o.TYPE_Q4_0, K):]
+    total = 0.0
+    for blk in range(nb):
+        scale = float(scales[blk])
+        for j in range(16):
+            byte = int(qs[16 * blk + j])
+            lo = (byte & 0x0F) - 8
+            hi = (byte >> 4) - 8
+            total += (lo * scale) * float(yf[32 * blk + 2 * j])
+            total += (hi * scale) * float(yf[32 * blk + 2 * j + 1])
+    return total
+
+
+def test_q4_0_pack_matches_page_scalar_kernel():
+    rng = np.random.default_rng(11)
+    K = 256
+    w = (rng.standard_normal((3, K)) * 0.02).astype(np.float32)
+    yf = rng.standard_normal(K)
+    packed, enc = o.encode_weights(o.TYPE_Q4_0, w)
+    deq = o.dequant_weights(o.TYPE_Q4_0, enc)
+    for n in range(3):
+        ref = float(deq[n] @ yf)
+        got = _page_q4_0_float_dot(packed[n], K, yf)
+        assert abs(got - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_q4_0_pack_nibble_order_is_pinned():
+    """A block whose codes differ between even and odd positions: swapping the
+    nibble order would change the page-kernel result."""
+    K = 32
+    x = np.zeros((1, K), dtype=np.float32)
+    x[0, 0::2] = 0.7
+    x[0, 1::2] = -0.1
+    x[0, 1] = -0.7
+    packed, enc = o.encode_weights(o.TYPE_Q4_0, x)
+    yf = np.zeros(K)
+    yf[0] = 1.0
+    got = _page_q4_0_float_dot(packed[0], K, yf)
+    assert got == pytest.approx(0.7, abs=1e-7)
+    yf[:] = 0
+    yf[1] = 1.0
+    assert _page_q4_0_float_dot(packed[0], K, yf) == pytest.approx(-0.7, abs=1e-7)
+
+
+# ---------------------------------------------------------------- helpers vs library routines
+
+def test_round_half_away_matches_decimal():
+    vals = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 0.49999997, -0.49999997, 126.5,
+            -126.5, 3.4999998, 7.5, -7.5, 0.0, -0.0, 1e-30, 127.0, 2.0 ** 40 + 0.5]
+    rng = np.random.default_rng(3)
+    vals += list(rng.uniform(-130, 130, 2000))
+    vals += list(np.round(rng.uniform(-130, 130, 200)) + 0.5)
+    got = o.round_half_away(np.array(vals, dtype=np.float64))
+    for v, g in zip(vals, got):
+        ref = float(Decimal(float(v)).quantize(Decimal(1), rounding=ROUND_HALF_UP))
+        assert g == ref, (v, g, ref)
+
+
+def test_f16_decode_matches_numpy_half():
+    bits = np.arange(0, 0x7C00, dtype=np.int64)
+    bits = np.concatenate([bits, bits | 0x8000])
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    got = o.f16_bits_to_f64(bits)
+    assert np.array_equal(got, ref)
+
+
+def test_f16_ceil_div_brute_force():
+    allbits = np.arange(0, 0x7C00, dtype=np.int64)
+    allvals = allbits.astype(np.uint16).view(np.float16).astype(np.float64)
+    rng = np.random.default_rng(5)
+    for c in (63, 945):
+        v = np.concatenate([
+            [0.0, 5.9604645e-08 * c, 1e-12, 1.0, c * 65504.0],
+            rng.uniform(0, 1, 300) ** 4 * 3.0,
+            allvals[rng.integers(1, len(allvals), 100)] * c,   # exact hits
+        ])
+        got = o.f16_ceil_div(v, c)
+        for vi, gi in zip(v, got):
+            ok = np.nonzero(c * allvals >= vi)[0]
+            assert gi == allbits[ok[0]], (c, vi)
