@@ -1,0 +1,79 @@
+"""Build libqblk.so (gfx950) in-tree with hipcc.
+
+    python -m block_quantized_qblk_amd.build_lib
+
+Objects go to <repo>/_build/, the shared library next to this file.
+"""
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libqblk.so")
+
+ARCH = "gfx950"
+
+SOURCES = [
+    "quantize_act.hip",
+    "pack_weights.hip",
+    "gemv.hip",
+    "gemm.hip",
+    "block_sums.hip",
+    "api.cpp",
+]
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+    f"--offload-arch={ARCH}",
+    # no packed-fp32 VALU instructions in generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep fp32 denormals (the quantizers' decisions must match IEEE)
+    "-fno-gpu-flush-denormals-to-zero",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", CSRC,
+]
+
+
+def hipcc():
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found; ROCm is required to build libqblk.so")
+    return exe
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
+    if src.endswith(".cpp"):
+        cmd += ["-x", "hip"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose=True):
+    """Compile every source and link libqblk.so. Always recompiles."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-o", tmp] + objs + [f"--offload-arch={ARCH}", "-fPIC"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}", file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,135 @@
+// C-ABI front end: argument validation, then one launch on the caller's
+// stream. Nothing is enqueued when validation fails. No allocation, no
+// synchronization, no state except a thread-local last HIP error.
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/qblk.h"
+#include "qblk_internal.h"
+
+#define QBLK_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool valid_type(int t) { return t == QBLK_Q4_0 || t == QBLK_Q8_0 || t == QBLK_Q4_K; }
+
+bool valid_k(int t, int64_t k) {
+  if (k <= 0) return false;
+  return t == QBLK_Q4_K ? (k % 256 == 0) : (k % 32 == 0);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// A dispatch holds fewer than 2^32 work-items per grid dimension.
+constexpr int64_t kMaxGridThreads = (int64_t{1} << 32) - 256;
+
+int finish(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return QBLK_ERR_LAUNCH;
+  }
+  return QBLK_OK;
+}
+
+// Shared validation of the product entry points.
+int check_product(int type, const void* wq, int64_t n, int64_t k, const void* xq, int64_t m,
+                  const void* out, int64_t ldy) {
+  if (!valid_type(type)) return QBLK_ERR_ARG;
+  if (n < 0 || m < 0) return QBLK_ERR_ARG;
+  if (!valid_k(type, k)) return QBLK_ERR_SHAPE;
+  if (n == 0 || m == 0) return QBLK_OK;
+  if (wq == nullptr || xq == nullptr || out == nullptr) return QBLK_ERR_ARG;
+  if (ldy < n) return QBLK_ERR_SHAPE;
+  if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(out, 4)) return QBLK_ERR_ALIGN;
+  return QBLK_OK;
+}
+
+}  // namespace
+
+QBLK_EXPORT int qblk_abi_version(void) { return QBLK_ABI_VERSION; }
+
+QBLK_EXPORT const char* qblk_strerror(int status) {
+  switch (status) {
+    case QBLK_OK: return "ok";
+    case QBLK_ERR_ARG: return "invalid argument (null pointer, negative size or unknown type)";
+    case QBLK_ERR_SHAPE: return "invalid shape (k not a positive multiple of the block size, or leading dimension too small)";
+    case QBLK_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case QBLK_ERR_UNSUPPORTED: return "size not supported by this entry point";
+    case QBLK_ERR_LAUNCH: return "HIP launch failed (see qblk_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+QBLK_EXPORT int qblk_last_hip_error(void) { return g_last_hip_error; }
+
+QBLK_EXPORT size_t qblk_weight_row_bytes(int type, int64_t k) {
+  if (!valid_type(type) || !valid_k(type, k)) return 0;
+  return static_cast<size_t>(qblk::row_bytes(type, k));
+}
+
+QBLK_EXPORT size_t qblk_weight_bytes(int type, int64_t n, int64_t k) {
+  if (n < 0) return 0;
+  return static_cast<size_t>(n) * qblk_weight_row_bytes(type, k);
+}
+
+QBLK_EXPORT size_t qblk_act_bytes(int64_t m, int64_t k) {
+  if (m < 0 || k <= 0 || k % 32 != 0) return 0;
+  return static_cast<size_t>(m * k + 8 * m * (k / 32));
+}
+
+QBLK_EXPORT int qblk_pack_weights(int type, const float* w, int64_t n, int64_t k, int64_t ldw,
+                                  void* wq, hipStream_t stream) {
+  if (!valid_type(type) || n < 0) return QBLK_ERR_ARG;
+  if (!valid_k(type, k)) return QBLK_ERR_SHAPE;
+  if (n == 0) return QBLK_OK;
+  if (w == nullptr || wq == nullptr) return QBLK_ERR_ARG;
+  if (ldw < k) return QBLK_ERR_SHAPE;
+  if (!aligned(w, 16) || ldw % 4 != 0 || !aligned(wq, 16)) return QBLK_ERR_ALIGN;
+  if (8 * n * (k / 32) > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(qblk::launch_pack_weights(type, w, n, k, ldw, wq, stream));
+}
+
+QBLK_EXPORT int qblk_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, void* xq,
+                                  hipStream_t stream) {
+  if (m < 0) return QBLK_ERR_ARG;
+  if (k <= 0 || k % 32 != 0) return QBLK_ERR_SHAPE;
+  if (m == 0) return QBLK_OK;
+  if (x == nullptr || xq == nullptr) return QBLK_ERR_ARG;
+  if (ldx < k) return QBLK_ERR_SHAPE;
+  if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(xq, 16)) return QBLK_ERR_ALIGN;
+  if (4 * m * (k / 32) > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(qblk::launch_quantize_act(x, m, k, ldx, xq, stream));
+}
+
+QBLK_EXPORT int qblk_gemv(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+                          int64_t batch, float* y, int64_t ldy, hipStream_t stream) {
+  const int st = check_product(type, wq, n, k, xq, batch, y, ldy);
+  if (st != QBLK_OK || n == 0 || batch == 0) return st;
+  if (batch > QBLK_GEMV_MAX_BATCH) return QBLK_ERR_UNSUPPORTED;
+  if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(qblk::launch_gemv(type, wq, n, k, xq, batch, y, ldy, stream));
+}
+
+QBLK_EXPORT int qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+                          int64_t m, float* y, int64_t ldy, hipStream_t stream) {
+  const int st = check_product(type, wq, n, k, xq, m, y, ldy);
+  if (st != QBLK_OK || n == 0 || m == 0) return st;
+  // grid: x = n / 128 workgroups of 256 work-items, y = m / 128 (<= 65535)
+  if (256 * ((n + 127) / 128) > kMaxGridThreads || (m + 127) / 128 > 65535)
+    return QBLK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(qblk::launch_gemm(type, wq, n, k, xq, m, y, ldy, stream));
+}
+
+QBLK_EXPORT int qblk_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+                                int64_t m, int32_t* sums, hipStream_t stream) {
+  const int st = check_product(type, wq, n, k, xq, m, sums, n);
+  if (st != QBLK_OK || n == 0 || m == 0) return st;
+  if (m * n * (k / 32) > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(qblk::launch_block_sums(type, wq, n, k, xq, m, sums, stream));
+}

@@ -1,0 +1,121 @@
+// Device-side building blocks shared by the GEMV, GEMM and block-sum
+// kernels: packed-row addressing, nibble unpack, int8 block dots and wave
+// reductions. gfx950 (CDNA4, wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qblk_internal.h"
+
+namespace qblk {
+
+// ---------------------------------------------------------------- loads
+// Weights are streamed exactly once per product: load them non-temporally so
+// they do not evict the activations that every wave re-reads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t load_stream4(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ uint4 load16(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---------------------------------------------------------------- fp16
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu));
+  return static_cast<float>(v);  // exact conversion
+}
+
+// ---------------------------------------------------------------- int8 dots
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int acc) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), acc, false);
+}
+
+// 32 4-bit codes (16 bytes, byte t = element 2t | element 2t+1 << 4) against
+// 32 int8 activation codes stored in the order 0,2,4,6,1,3,5,7 per group of
+// 8: the low nibbles of four bytes are elements 0,2,4,6 of the group, the
+// high nibbles elements 1,3,5,7, so each dword dot needs no permute.
+// Nibbles are taken as unsigned 0..15 (non-negative int8).
+__device__ __forceinline__ int dot_nib32(uint4 w, uint4 a0, uint4 a1, int acc) {
+  const uint32_t m = 0x0F0F0F0Fu;
+  acc = dot4(w.x & m, a0.x, acc);
+  acc = dot4((w.x >> 4) & m, a0.y, acc);
+  acc = dot4(w.y & m, a0.z, acc);
+  acc = dot4((w.y >> 4) & m, a0.w, acc);
+  acc = dot4(w.z & m, a1.x, acc);
+  acc = dot4((w.z >> 4) & m, a1.y, acc);
+  acc = dot4(w.w & m, a1.z, acc);
+  acc = dot4((w.w >> 4) & m, a1.w, acc);
+  return acc;
+}
+
+// 32 int8 codes against 32 int8 codes, both in the same per-group order.
+__device__ __forceinline__ int dot_i8x32(uint4 w0, uint4 w1, uint4 a0, uint4 a1, int acc) {
+  acc = dot4(w0.x, a0.x, acc);
+  acc = dot4(w0.y, a0.y, acc);
+  acc = dot4(w0.z, a0.z, acc);
+  acc = dot4(w0.w, a0.w, acc);
+  acc = dot4(w1.x, a1.x, acc);
+  acc = dot4(w1.y, a1.y, acc);
+  acc = dot4(w1.z, a1.z, acc);
+  acc = dot4(w1.w, a1.w, acc);
+  return acc;
+}
+
+// Q4_K header of one super-block: fp16 d, fp16 d_min, then sc_j at bits
+// [6j, 6j+6) and mn_j at bits [48+6j, 48+6j+6) of the 96-bit field held in
+// h.y (bits 0..31), h.z (32..63), h.w (64..95).
+__device__ __forceinline__ uint32_t q4k_sc(uint4 h, int j) {
+  const uint64_t lo = (static_cast<uint64_t>(h.z) << 32) | h.y;
+  return static_cast<uint32_t>(lo >> (6 * j)) & 63u;
+}
+__device__ __forceinline__ uint32_t q4k_mn(uint4 h, int j) {
+  const uint64_t hi = (static_cast<uint64_t>(h.w) << 32) | h.z;
+  return static_cast<uint32_t>(hi >> (16 + 6 * j)) & 63u;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Activation buffer views (m rows of k): codes, then (d, sum) pairs.
+struct ActView {
+  const uint8_t* q;   // [m][k] int8 codes
+  const uint8_t* ds;  // [m][nb] (fp32 d, int32 sum)
+  int64_t k;
+  int64_t nb;
+  __device__ __forceinline__ const uint8_t* codes(int64_t row, int64_t blk) const {
+    return q + row * k + 32 * blk;
+  }
+  __device__ __forceinline__ float2 dsum(int64_t row, int64_t blk) const {
+    return *reinterpret_cast<const float2*>(ds + 8 * (row * nb + blk));
+  }
+};
+
+__host__ __device__ inline ActView make_act(const void* xq, int64_t m, int64_t k) {
+  ActView a;
+  a.q = static_cast<const uint8_t*>(xq);
+  a.ds = a.q + m * k;
+  a.k = k;
+  a.nb = k / 32;
+  return a;
+}
+
+// Packed weight row views.
+struct WeightView {
+  const uint8_t* base;
+  int64_t row_bytes;
+  int64_t hdr_bytes;
+  __device__ __forceinline__ const uint8_t* row(int64_t n) const { return base + n * row_bytes; }
+};
+
+}  // namespace qblk

@@ -1,0 +1,48 @@
+// Host-side declarations shared between the C-ABI front end (api.cpp) and
+// the kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qblk {
+
+enum : int { kQ4_0 = 1, kQ8_0 = 2, kQ4_K = 3 };
+
+inline int64_t pad16(int64_t v) { return (v + 15) / 16 * 16; }
+
+// Header region bytes of one packed row (scales, padded to 16 B).
+inline int64_t header_bytes(int type, int64_t k) {
+  switch (type) {
+    case kQ4_0:
+    case kQ8_0: return pad16(4 * (k / 32));
+    case kQ4_K: return 16 * (k / 256);
+    default: return 0;
+  }
+}
+
+// Bytes of one packed row.
+inline int64_t row_bytes(int type, int64_t k) {
+  switch (type) {
+    case kQ4_0: return header_bytes(type, k) + 16 * (k / 32);
+    case kQ8_0: return header_bytes(type, k) + 32 * (k / 32);
+    case kQ4_K: return header_bytes(type, k) + 128 * (k / 256);
+    default: return 0;
+  }
+}
+
+// Launchers (validated arguments only). Each returns the hipError_t of the
+// launch.
+hipError_t launch_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, void* xq,
+                               hipStream_t s);
+hipError_t launch_pack_weights(int type, const float* w, int64_t n, int64_t k, int64_t ldw,
+                               void* wq, hipStream_t s);
+hipError_t launch_gemv(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+                       int64_t batch, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+                       int64_t m, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+                             int64_t m, int32_t* sums, hipStream_t s);
+
+}  // namespace qblk

@@ -1,0 +1,195 @@
+"""Python binding of libqblk.so (ctypes). Argument marshalling only: every
+step of the product runs in the library's HIP kernels. torch supplies device
+memory and the current stream.
+
+Function names match the C ABI in include/qblk.h.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqblk.so")
+
+Q4_0, Q8_0, Q4_K = 1, 2, 3
+TYPES = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K}
+GEMV_MAX_BATCH = 64
+
+_lib = None
+
+
+class QblkError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({strerror(status)})")
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        # build once from source; a failure here is an error, there is no
+        # fallback path
+        from . import build_lib
+        build_lib.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    sig = {
+        "qblk_abi_version": (i32, []),
+        "qblk_strerror": (ctypes.c_char_p, [i32]),
+        "qblk_last_hip_error": (i32, []),
+        "qblk_weight_row_bytes": (ctypes.c_size_t, [i32, i64]),
+        "qblk_weight_bytes": (ctypes.c_size_t, [i32, i64, i64]),
+        "qblk_act_bytes": (ctypes.c_size_t, [i64, i64]),
+        "qblk_pack_weights": (i32, [i32, vp, i64, i64, i64, vp, vp]),
+        "qblk_quantize_act": (i32, [vp, i64, i64, i64, vp, vp]),
+        "qblk_gemv": (i32, [i32, vp, i64, i64, vp, i64, vp, i64, vp]),
+        "qblk_gemm": (i32, [i32, vp, i64, i64, vp, i64, vp, i64, vp]),
+        "qblk_block_sums": (i32, [i32, vp, i64, i64, vp, i64, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def lib():
+    return _load()
+
+
+def _type(t):
+    if isinstance(t, str):
+        return TYPES[t]
+    return int(t)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _check(status, what):
+    if status != 0:
+        raise QblkError(status, what)
+
+
+def _require_cuda(t, name, rows=False):
+    """Device tensor, contiguous (or, with rows=True, unit stride inside each
+    row so that stride(0) can be passed as the leading dimension)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if rows:
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be 2-D with unit stride along rows")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------- sizes
+
+def abi_version():
+    return _load().qblk_abi_version()
+
+
+def strerror(status):
+    return _load().qblk_strerror(int(status)).decode()
+
+
+def qblk_weight_row_bytes(wtype, k):
+    return int(_load().qblk_weight_row_bytes(_type(wtype), int(k)))
+
+
+def qblk_weight_bytes(wtype, n, k):
+    return int(_load().qblk_weight_bytes(_type(wtype), int(n), int(k)))
+
+
+def qblk_act_bytes(m, k):
+    return int(_load().qblk_act_bytes(int(m), int(k)))
+
+
+# ---------------------------------------------------------------- entry points
+
+def qblk_pack_weights(wtype, w, out=None, stream=None):
+    """Quantize fp32 weights w [n, k] (device) into a packed uint8 buffer."""
+    import torch
+    _require_cuda(w, "w", rows=True)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    n, k = w.shape
+    t = _type(wtype)
+    nbytes = qblk_weight_bytes(t, n, k)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+    elif out.numel() < nbytes:
+        raise ValueError("out too small")
+    _check(_load().qblk_pack_weights(t, _ptr(w), n, k, w.stride(0), _ptr(out), _stream(stream)),
+           "qblk_pack_weights")
+    return out
+
+
+def qblk_quantize_act(x, out=None, stream=None):
+    """Quantize fp32 activations x [m, k] (device) into an activation buffer."""
+    import torch
+    _require_cuda(x, "x", rows=True)
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be a 2-D float32 tensor")
+    m, k = x.shape
+    nbytes = qblk_act_bytes(m, k)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    elif out.numel() < nbytes:
+        raise ValueError("out too small")
+    _check(_load().qblk_quantize_act(_ptr(x), m, k, x.stride(0), _ptr(out), _stream(stream)),
+           "qblk_quantize_act")
+    return out
+
+
+def _product(fname, wtype, wq, n, k, xq, m, y, stream):
+    import torch
+    _require_cuda(wq, "wq")
+    _require_cuda(xq, "xq")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=wq.device)
+    _require_cuda(y, "y", rows=True)
+    if y.dtype != torch.float32 or y.dim() != 2 or y.shape[0] < m or y.shape[1] < n:
+        raise ValueError("y must be float32 [m, >= n]")
+    if wq.numel() < qblk_weight_bytes(wtype, n, k) or xq.numel() < qblk_act_bytes(m, k):
+        raise ValueError("wq or xq smaller than the packed sizes")
+    fn = getattr(_load(), fname)
+    _check(fn(_type(wtype), _ptr(wq), int(n), int(k), _ptr(xq), int(m), _ptr(y), y.stride(0),
+              _stream(stream)), fname)
+    return y
+
+
+def qblk_gemv(wtype, wq, n, k, xq, batch=1, y=None, stream=None):
+    """y[b, :n] = W x_b for b < batch (decode path, batch <= 64)."""
+    return _product("qblk_gemv", wtype, wq, n, k, xq, batch, y, stream)
+
+
+def qblk_gemm(wtype, wq, n, k, xq, m, y=None, stream=None):
+    """Y[m, :n] = X W^T (prefill path, int8 matrix cores)."""
+    return _product("qblk_gemm", wtype, wq, n, k, xq, m, y, stream)
+
+
+def qblk_block_sums(wtype, wq, n, k, xq, m, out=None, stream=None):
+    """int32 [m, n, k/32] integer block sums (test export)."""
+    import torch
+    _require_cuda(wq, "wq")
+    _require_cuda(xq, "xq")
+    if out is None:
+        out = torch.empty((m, n, k // 32), dtype=torch.int32, device=wq.device)
+    _require_cuda(out, "out")
+    if out.numel() < m * n * (k // 32):
+        raise ValueError("out too small")
+    _check(_load().qblk_block_sums(_type(wtype), _ptr(wq), int(n), int(k), _ptr(xq), int(m),
+                                   _ptr(out), _stream(stream)), "qblk_block_sums")
+    return out

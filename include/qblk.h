@@ -1,0 +1,183 @@
+/*
+ * qblk.h — C ABI of the block-quantized weight x activation product for
+ * MI355X (gfx950).
+ *
+ * What is computed (pages cited by title and section):
+ *   - Weights are quantized in 32-element blocks with one scale per block
+ *     ("llama.cpp 推理引擎", §5.1 symmetric quantization, §5.3 Q4_0, §5.4 Q8_0)
+ *     or in 256-element super-blocks of 8 sub-blocks with per-sub-block scale
+ *     and min codes under fp16 super-block scales ("llama.cpp 推理引擎", §5.5
+ *     K-quant; "llama.cpp：一个人、一个周末、一个改变 AI 推理格局的 C++ 文件",
+ *     section 量化是怎么做到的？).
+ *   - Activations are quantized on the fly to int8 32-blocks with an fp32
+ *     scale (the §5.1 rule at 8 bits).
+ *   - Inside each 32-block the dot product is integer (wmrh.cn "bare engine"
+ *     article, §2.2: int4 x int8 multiply-add); the scales are applied
+ *     outside it in fp32 ("llama.cpp 推理引擎", §6.4).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named w, x, y, wq, xq, sums are DEVICE pointers owned by the
+ *     caller. The library never allocates, frees or synchronizes, and keeps
+ *     no state between calls except a thread-local last HIP error code.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without waiting. Calls are reentrant and thread-safe.
+ *   - Every argument is validated BEFORE anything is enqueued; on any error
+ *     nothing is enqueued and a negative qblk_status is returned.
+ *   - Sizes are element counts (int64_t). m, n or batch equal to 0 is a valid
+ *     empty call that enqueues nothing and returns QBLK_OK. Negative sizes are
+ *     QBLK_ERR_ARG.
+ *   - Buffers must not overlap unless stated.
+ *
+ * Byte layouts (little-endian; nb = k/32, nsb = k/256; a "row" is one output
+ * channel n of the weight matrix W[n][k]):
+ *   Q4_0 row : [fp32 d x nb, zero-padded to a multiple of 16 B]
+ *              [16 B x nb: byte t of block b = (q[32b+2t]+8) | (q[32b+2t+1]+8) << 4]
+ *              codes q in [-7, 7] when packed by this library; any nibble
+ *              0..15 decodes as nibble - 8.
+ *   Q8_0 row : [fp32 d x nb, zero-padded to a multiple of 16 B]
+ *              [32 int8 x nb; inside a block each group of 8 codes is stored
+ *               in the element order 0,2,4,6,1,3,5,7]
+ *   Q4_K row : [16 B header x nsb][128 B x nsb]
+ *              header = fp16 d, fp16 d_min (<= 0), 12 bytes holding a 96-bit
+ *              little-endian field with sc_j at bits [6j, 6j+6) and mn_j at
+ *              bits [48+6j, 48+6j+6), j = 0..7;
+ *              sub-block j of a super-block is bytes [16j, 16j+16) of its 128,
+ *              byte t = q[32j+2t] | q[32j+2t+1] << 4, q in 0..15;
+ *              weight value = (d*sc_j)*q + d_min*mn_j.
+ *   Rows are stored back to back; qblk_weight_row_bytes gives the stride.
+ *   Activation buffer (m rows, opaque to callers but fixed):
+ *              [m*k int8 codes, row-major; inside each 32-block the groups
+ *               of 8 use the order 0,2,4,6,1,3,5,7]
+ *              [m*nb pairs (fp32 scale d, int32 sum of the block's 32 codes)]
+ *
+ * Alignment: wq, xq and x must be 16-byte aligned and ldx a multiple of 4;
+ * y, sums and w need 4-byte alignment (w 16-byte, ldw a multiple of 4).
+ */
+#ifndef QBLK_H
+#define QBLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QBLK_ABI_VERSION 1
+
+typedef enum {
+  QBLK_Q4_0 = 1, /* 32-blocks, 4-bit codes, fp32 scale: 20 B / 32 weights */
+  QBLK_Q8_0 = 2, /* 32-blocks, int8 codes, fp32 scale: 36 B / 32 weights  */
+  QBLK_Q4_K = 3  /* 256-element super-blocks, 144 B / 256 weights         */
+} qblk_type;
+
+typedef enum {
+  QBLK_OK = 0,
+  QBLK_ERR_ARG = -1,         /* null pointer, negative size, unknown type    */
+  QBLK_ERR_SHAPE = -2,       /* k not a positive multiple of 32 (256 for
+                                Q4_K), or a leading dimension too small      */
+  QBLK_ERR_ALIGN = -3,       /* pointer or leading dimension misaligned      */
+  QBLK_ERR_UNSUPPORTED = -4, /* size beyond what a kernel supports (e.g.
+                                gemv batch > QBLK_GEMV_MAX_BATCH)            */
+  QBLK_ERR_LAUNCH = -5       /* the HIP launch failed; see
+                                qblk_last_hip_error()                        */
+} qblk_status;
+
+#define QBLK_GEMV_MAX_BATCH 64
+
+/* Returns QBLK_ABI_VERSION of the loaded library. */
+int qblk_abi_version(void);
+
+/* Human-readable text for a qblk_status value (static storage). */
+const char *qblk_strerror(int status);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int qblk_last_hip_error(void);
+
+/* Bytes of one packed weight row of k elements (0 if type or k is invalid). */
+size_t qblk_weight_row_bytes(int type, int64_t k);
+
+/* Bytes of a packed n x k weight matrix = n * qblk_weight_row_bytes (0 if
+ * invalid). */
+size_t qblk_weight_bytes(int type, int64_t n, int64_t k);
+
+/* Bytes of the activation buffer for m rows of k elements (0 if invalid):
+ * m*k + 8*m*(k/32). */
+size_t qblk_act_bytes(int64_t m, int64_t k);
+
+/*
+ * Weight quantization and packing (setup step).
+ * "llama.cpp 推理引擎" §5.1 (symmetric rule; Q4_0 at 4 bits with codes in
+ * [-7, 7], Q8_0 at 8 bits), §5.2 + §5.5 (Q4_K: asymmetric sub-blocks under
+ * fp16 super-block scales).
+ *   w   : fp32 [n][ldw], row n holds the k weights of output channel n.
+ *   wq  : out, qblk_weight_bytes(type, n, k) bytes, layout above.
+ * Rounding is half away from zero. Q4_0/Q8_0 decisions are taken in fp32
+ * with IEEE division; Q4_K decisions in fp64:
+ *   m_j  = max(0, -min of sub-block j); d_min = -(smallest fp16 h with
+ *   63*h >= max_j m_j); mn_j = smallest code with mn_j*h >= m_j;
+ *   t_j  = max of sub-block j + mn_j*h; d = smallest fp16 with
+ *   945*d >= max_j t_j; sc_j = smallest code with 15*sc_j*d >= t_j;
+ *   q = clamp(round((x + mn_j*h) / (sc_j*d)), 0, 15) (0 when sc_j*d == 0).
+ * Inputs must be finite; a super-block whose range exceeds what fp16 d can
+ * express saturates d at 65504.
+ * Errors: QBLK_ERR_ARG (null, negative n, unknown type), QBLK_ERR_SHAPE
+ * (k invalid, ldw < k), QBLK_ERR_ALIGN, QBLK_ERR_LAUNCH.
+ */
+int qblk_pack_weights(int type, const float *w, int64_t n, int64_t k,
+                      int64_t ldw, void *wq, hipStream_t stream);
+
+/*
+ * On-the-fly activation quantization: "llama.cpp 推理引擎" §5.1 at 8 bits,
+ * per row and per 32 consecutive elements: d = max|x| / 127 (IEEE fp32
+ * division), q = round_half_away(x / d) (IEEE fp32 division), d == 0 gives
+ * q == 0; the int32 sum of the 32 codes is stored beside d.
+ *   x  : fp32 [m][ldx].
+ *   xq : out, qblk_act_bytes(m, k) bytes, layout above.
+ * Errors: QBLK_ERR_ARG, QBLK_ERR_SHAPE (k % 32 != 0, k <= 0, ldx < k),
+ * QBLK_ERR_ALIGN, QBLK_ERR_LAUNCH.
+ */
+int qblk_quantize_act(const float *x, int64_t m, int64_t k, int64_t ldx,
+                      void *xq, hipStream_t stream);
+
+/*
+ * Decode-path product (few activation rows): for b < batch, n < n:
+ *   y[b*ldy + n] = sum over 32-blocks j of
+ *     Q4_0/Q8_0: dw[n][j] * dx[b][j] * S[b][n][j]
+ *     Q4_K     : dx[b][j] * ((d*sc_j)[n] * S[b][n][j] + (d_min*mn_j)[n] * A[b][j])
+ *   where S is the integer dot of block j's weight codes (Q4_0: nibble - 8,
+ *   Q8_0: int8, Q4_K: nibble) with the activation codes, and A the
+ *   activation block sum. Accumulation is fp32 in an unspecified order.
+ *   wq : packed weights [n] rows of k;  xq : activation buffer of `batch`
+ *   rows of k (from qblk_quantize_act);  y : fp32 [batch][ldy].
+ * Errors: QBLK_ERR_ARG, QBLK_ERR_SHAPE (k invalid, ldy < n when batch > 1),
+ * QBLK_ERR_ALIGN, QBLK_ERR_UNSUPPORTED (batch > QBLK_GEMV_MAX_BATCH),
+ * QBLK_ERR_LAUNCH.
+ */
+int qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void *xq,
+              int64_t batch, float *y, int64_t ldy, hipStream_t stream);
+
+/*
+ * Prefill-path product: the same result as qblk_gemv for m activation rows,
+ * Y[m][ldy] = X * W^T, computed with int8 matrix-core tiles. Any m >= 0.
+ * Errors as qblk_gemv (no batch limit).
+ */
+int qblk_gemm(int type, const void *wq, int64_t n, int64_t k, const void *xq,
+              int64_t m, float *y, int64_t ldy, hipStream_t stream);
+
+/*
+ * Test export: the integer block sums S[mm][nn][j] (int32, layout
+ * [m][n][k/32]) that qblk_gemv / qblk_gemm scale and accumulate, computed
+ * with the same device unpack and dot code. Intended for small shapes.
+ * Errors as qblk_gemv (no batch limit).
+ */
+int qblk_block_sums(int type, const void *wq, int64_t n, int64_t k,
+                    const void *xq, int64_t m, int32_t *sums,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QBLK_H */

@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+exactly the functions include/qblk.h declares, its size functions match the
+oracle's layouts, and invalid arguments are rejected with the documented
+status before anything is launched. No compute call is made here."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from block_quantized_qblk_amd import qblk
+from oracle import qblk_oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qblk.h")
+
+OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+
+# plausible 256-byte aligned device addresses that are never dereferenced
+# (validation fails before any launch in every call below)
+FAKE = 0x7F0000000000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qblk_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_reports_abi():
+    lib = qblk.lib()
+    assert lib.qblk_abi_version() == 1
+    assert qblk.strerror(0) == "ok"
+    assert "shape" in qblk.strerror(-2)
+
+
+def test_exports_match_header():
+    declared = _declared()
+    assert len(declared) >= 10
+    lib = qblk.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", qblk.LIB_PATH],
+                             capture_output=True, text=True, check=True).stdout
+        exported = sorted(set(re.findall(r"\b[TW] (qblk_\w+)", out)))
+        assert exported == declared
+
+
+@pytest.mark.parametrize("k", [32, 96, 256, 416, 1024, 4096, 14336, 28672])
+def test_size_functions_match_oracle(k):
+    for t in (o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K):
+        if t == o.TYPE_Q4_K and k % 256:
+            assert qblk.qblk_weight_row_bytes(t, k) == 0
+            continue
+        assert qblk.qblk_weight_row_bytes(t, k) == o.row_bytes(t, k)
+        assert qblk.qblk_weight_bytes(t, 37, k) == 37 * o.row_bytes(t, k)
+        assert qblk.qblk_weight_row_bytes(t, k) % 16 == 0
+    assert qblk.qblk_act_bytes(5, k) == o.act_bytes(5, k)
+
+
+def test_size_functions_reject_invalid():
+    assert qblk.qblk_weight_row_bytes(0, 256) == 0
+    assert qblk.qblk_weight_row_bytes(o.TYPE_Q4_0, 48) == 0
+    assert qblk.qblk_weight_row_bytes(o.TYPE_Q4_0, 0) == 0
+    assert qblk.qblk_weight_bytes(o.TYPE_Q8_0, -1, 256) == 0
+    assert qblk.qblk_act_bytes(1, 33) == 0
+    assert qblk.qblk_act_bytes(-1, 32) == 0
+    assert qblk.qblk_act_bytes(0, 32) == 0
+
+
+def _p(addr):
+    return ctypes.c_void_p(addr)
+
+
+NULL = ctypes.c_void_p(0)
+
+
+def test_product_argument_validation():
+    lib = qblk.lib()
+    for fname in ("qblk_gemv", "qblk_gemm"):
+        f = getattr(lib, fname)
+        w, x, y = _p(FAKE), _p(FAKE + 0x100000), _p(FAKE + 0x200000)
+        assert f(9, w, 16, 256, x, 1, y, 16, NULL) == ERR_ARG          # unknown type
+        assert f(3, w, -1, 256, x, 1, y, 16, NULL) == ERR_ARG          # negative n
+        assert f(3, w, 16, 256, x, -2, y, 16, NULL) == ERR_ARG         # negative m
+        assert f(3, w, 16, 288, x, 1, y, 16, NULL) == ERR_SHAPE        # Q4_K k % 256
+        assert f(1, w, 16, 48, x, 1, y, 16, NULL) == ERR_SHAPE         # k % 32
+        assert f(2, w, 16, 0, x, 1, y, 16, NULL) == ERR_SHAPE          # k == 0
+        assert f(3, NULL, 16, 256, x, 1, y, 16, NULL) == ERR_ARG       # null wq
+        assert f(3, w, 16, 256, NULL, 1, y, 16, NULL) == ERR_ARG       # null xq
+        assert f(3, w, 16, 256, x, 1, NULL, 16, NULL) == ERR_ARG       # null y
+        assert f(3, w, 16, 256, x, 1, y, 15, NULL) == ERR_SHAPE        # ldy < n
+        assert f(3, _p(FAKE + 8), 16, 256, x, 1, y, 16, NULL) == ERR_ALIGN
+        assert f(3, w, 16, 256, _p(FAKE + 4), 1, y, 16, NULL) == ERR_ALIGN
+        assert f(3, w, 16, 256, x, 1, _p(FAKE + 2), 16, NULL) == ERR_ALIGN
+        # empty calls are valid no-ops, even with null pointers
+        assert f(3, NULL, 0, 256, NULL, 1, NULL, 0, NULL) == OK
+        assert f(3, NULL, 16, 256, NULL, 0, NULL, 16, NULL) == OK
+    assert lib.qblk_gemv(3, _p(FAKE), 16, 256, _p(FAKE), 65, _p(FAKE), 16, NULL) == ERR_UNSUPPORTED
+    assert lib.qblk_gemm(3, _p(FAKE), 16, 256, _p(FAKE), 65536 * 128, _p(FAKE), 16,
+                         NULL) == ERR_UNSUPPORTED
+
+
+def test_quantize_and_pack_argument_validation():
+    lib = qblk.lib()
+    x, xq = _p(FAKE), _p(FAKE + 0x100000)
+    q = lib.qblk_quantize_act
+    assert q(x, -1, 256, 256, xq, NULL) == ERR_ARG
+    assert q(x, 2, 100, 256, xq, NULL) == ERR_SHAPE
+    assert q(x, 2, 256, 255, xq, NULL) == ERR_SHAPE
+    assert q(x, 2, 256, 258, xq, NULL) == ERR_ALIGN
+    assert q(_p(FAKE + 4), 2, 256, 256, xq, NULL) == ERR_ALIGN
+    assert q(x, 2, 256, 256, _p(FAKE + 8), NULL) == ERR_ALIGN
+    assert q(NULL, 2, 256, 256, xq, NULL) == ERR_ARG
+    assert q(NULL, 0, 256, 256, NULL, NULL) == OK
+    p = lib.qblk_pack_weights
+    assert p(5, x, 4, 256, 256, xq, NULL) == ERR_ARG
+    assert p(3, x, 4, 32, 32, xq, NULL) == ERR_SHAPE
+    assert p(1, x, 4, 32, 16, xq, NULL) == ERR_SHAPE
+    assert p(1, x, 4, 32, 34, xq, NULL) == ERR_ALIGN
+    assert p(2, x, 4, 32, 32, _p(FAKE + 4), NULL) == ERR_ALIGN
+    assert p(2, x, -4, 32, 32, xq, NULL) == ERR_ARG
+    assert p(2, NULL, 0, 32, 32, NULL, NULL) == OK
+    b = lib.qblk_block_sums
+    assert b(3, x, 4, 256, xq, 2, NULL, NULL) == ERR_ARG
+    assert b(3, x, 4, 200, xq, 2, _p(FAKE), NULL) == ERR_SHAPE

@@ -1,0 +1,302 @@
+"""GPU parity: every entry point, called through the C ABI, against the
+oracle. Integer work (activation codes, packed bytes, block sums) must be
+bit-exact; fp32 outputs within REL_TOL = 1e-5 (max-normalized)."""
+
+import numpy as np
+import pytest
+
+from block_quantized_qblk_amd import qblk, synth
+from oracle import qblk_oracle as o
+from tests.gpu_util import (REL_TOL, check_rel, dev, dev_pack, dev_quantize, expected, host,
+                            oracle_act, torch)
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K]
+TNAME = {1: "Q4_0", 2: "Q8_0", 3: "Q4_K"}
+
+
+def _special_rows(rng, n, k, std=0.02):
+    """Seeded weights with zero, constant, single-non-zero and outlier blocks."""
+    w = (rng.standard_normal((n, k)) * std).astype(np.float32)
+    w[0, :32] = 0
+    if k >= 64:
+        w[0, 32:64] = 0.011
+    if n > 1 and k >= 256:
+        w[1, :256] = 0
+        w[1, 7] = -0.3
+    if n > 2:
+        w[2] = np.abs(w[2])
+    idx = rng.choice(n * k, size=max(1, n * k // 1000), replace=False)
+    w.reshape(-1)[idx] = np.where(rng.random(idx.size) < 0.5, -0.2, 0.2)
+    return w
+
+
+# ================================================================ activation quantization
+
+@pytest.mark.parametrize("m,k", [(1, 4096), (3, 1184), (7, 32), (512, 4096), (2, 14336)])
+def test_quantize_act_bit_exact(m, k):
+    print(f"quantize_act m={m} k={k}", flush=True)
+    x = synth.activations(1000 + m, m, k)
+    x[0, :32] = 0
+    if k >= 64:
+        x[-1, 32:64] = 3.0
+    got = host(dev_quantize(x))
+    ref = o.pack_act(*oracle_act(x))
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_act_ties_and_denormals():
+    print("quantize_act ties/denormals", flush=True)
+    x = np.zeros((1, 128), dtype=np.float32)
+    # block 0: d = 127/127 = 1, ties x.5 must round away from zero
+    x[0, :8] = [127.0, 2.5, -2.5, 0.5, -0.5, 126.5, -3.5, 1.4999999]
+    # block 1: tiny normal amax -> subnormal d
+    x[0, 32:40] = np.float32(1e-38) * np.array([1, -0.5, 0.25, 0.75, -1, 0.1, 0, 0.3], np.float32)
+    # block 2: subnormal inputs
+    x[0, 64:70] = np.float32(1e-42) * np.array([1, 2, -3, 4, -5, 6], np.float32)
+    # block 3: huge values
+    x[0, 96:100] = [3e38, -1e38, 1e30, -3e38]
+    got = host(dev_quantize(x))
+    q, d, s = oracle_act(x)
+    assert q[0, 1] == 3 and q[0, 2] == -3 and q[0, 3] == 1 and q[0, 4] == -1
+    assert np.array_equal(got, o.pack_act(q, d, s))
+
+
+def test_quantize_act_strided_rows():
+    print("quantize_act strided", flush=True)
+    big = synth.activations(7, 5, 640)
+    xs = dev(big)[:, 64:64 + 512]
+    got = host(qblk.qblk_quantize_act(xs))
+    assert np.array_equal(got, o.pack_act(*oracle_act(big[:, 64:576])))
+
+
+# ================================================================ weight packing
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("n,k", [(37, 1024), (5, 256), (64, 4096), (3, 2304)])
+def test_pack_weights_bit_exact(wtype, n, k):
+    print(f"pack {TNAME[wtype]} n={n} k={k}", flush=True)
+    rng = np.random.default_rng(50 * wtype + n)
+    w = _special_rows(rng, n, k)
+    got = host(dev_pack(wtype, w)).reshape(n, -1)
+    ref, _ = o.encode_weights(wtype, w)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("wtype", [o.TYPE_Q4_0, o.TYPE_Q8_0])
+def test_pack_weights_padded_header(wtype):
+    """k = 416: 13 blocks, 52 header bytes padded to 64."""
+    print(f"pack padded {TNAME[wtype]}", flush=True)
+    rng = np.random.default_rng(3)
+    w = _special_rows(rng, 9, 416)
+    buf = torch().full((qblk.qblk_weight_bytes(wtype, 9, 416),), 0xAB, dtype=torch().uint8,
+                       device="cuda")
+    qblk.qblk_pack_weights(wtype, dev(w), out=buf)
+    ref, _ = o.encode_weights(wtype, w)
+    assert np.array_equal(host(buf).reshape(9, -1), ref)
+
+
+def test_pack_q4_k_extreme_ranges():
+    """Tiny, huge and single-signed super-blocks."""
+    print("pack Q4_K extremes", flush=True)
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    w[0] *= 1e-6                      # d in the fp16 subnormal range
+    w[1] *= 1e3                       # large scales
+    w[2] = np.abs(w[2]) + 0.5         # all positive: no min term
+    w[3] = -np.abs(w[3]) - 0.5        # all negative
+    w[4, :256] = 0.0                  # zero super-block
+    w[5, ::2] = 0.0
+    got = host(dev_pack(o.TYPE_Q4_K, w)).reshape(6, -1)
+    ref, enc = o.encode_weights(o.TYPE_Q4_K, w)
+    assert np.array_equal(got, ref)
+
+
+# ================================================================ block sums
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("m,n,k", [(1, 1, 256), (3, 37, 512), (5, 7, 2304)])
+def test_block_sums_bit_exact(wtype, m, n, k):
+    print(f"block_sums {TNAME[wtype]} m={m} n={n} k={k}", flush=True)
+    rng = np.random.default_rng(7 * wtype + m)
+    w = _special_rows(rng, n, k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    sums = qblk.qblk_block_sums(wtype, dev_pack(wtype, w), n, k, dev_quantize(x), m)
+    _, enc = o.encode_weights(wtype, w)
+    aq, _, _ = oracle_act(x)
+    ref = o.block_sums(o.weight_codes_for_sums(wtype, enc), aq)
+    assert np.array_equal(host(sums).astype(np.int64), ref)
+
+
+# ================================================================ exact-arithmetic products
+
+def _exact_case(wtype, n, k, m, seed):
+    """Codes and power-of-two scales chosen so that every fp32 step of the
+    product is exact: the device result must equal the oracle bit for bit,
+    which pins the integer block sums inside the production kernels."""
+    rng = np.random.default_rng(seed)
+    nb = k // 32
+    if wtype == o.TYPE_Q4_K:
+        enc = dict(d_bits=np.full((n, k // 256), 0x1C00, np.uint16),       # 2^-8
+                   dmin_bits=np.full((n, k // 256), 0x9800, np.uint16),    # -2^-9
+                   sc=rng.integers(0, 8, (n, k // 256, 8)),
+                   mn=rng.integers(0, 64, (n, k // 256, 8)),
+                   q=rng.integers(0, 16, (n, k)))
+        packed = o.pack_q4_k(enc)
+    elif wtype == o.TYPE_Q4_0:
+        enc = dict(q=rng.integers(-8, 8, (n, k)), d=np.full((n, nb), 2.0 ** -6, np.float32))
+        packed = o.pack_q4_0(enc["q"], enc["d"])
+    else:
+        enc = dict(q=rng.integers(-12, 13, (n, k)), d=np.full((n, nb), 2.0 ** -7, np.float32))
+        packed = o.pack_q8_0(enc["q"], enc["d"])
+    a = rng.integers(-8, 9, (m, k))
+    a[:, ::32] = 127 * np.where(rng.random((m, nb)) < 0.5, -1, 1)
+    x = (a * 0.25).astype(np.float32)
+    act = oracle_act(x)
+    assert np.array_equal(act[0], a)
+    y32, y64 = o.product(wtype, enc, act)
+    assert np.array_equal(y32.astype(np.float64), y64)   # exact in fp32
+    return packed, x, y32
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("batch", [1, 3, 8, 11])
+def test_gemv_exact_arithmetic(wtype, batch):
+    print(f"gemv exact {TNAME[wtype]} batch={batch}", flush=True)
+    n, k = 67, 2304 if wtype == o.TYPE_Q4_K else 2336
+    packed, x, y32 = _exact_case(wtype, n, k, batch, 900 + wtype)
+    y = qblk.qblk_gemv(wtype, dev(packed.reshape(-1)), n, k, dev_quantize(x), batch)
+    assert np.array_equal(host(y), y32)
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("m", [1, 37, 130])
+def test_gemm_exact_arithmetic(wtype, m):
+    print(f"gemm exact {TNAME[wtype]} m={m}", flush=True)
+    n, k = 150, 1024 if wtype == o.TYPE_Q4_K else 1056
+    packed, x, y32 = _exact_case(wtype, n, k, m, 700 + wtype + m)
+    y = qblk.qblk_gemm(wtype, dev(packed.reshape(-1)), n, k, dev_quantize(x), m)
+    assert np.array_equal(host(y), y32)
+
+
+# ================================================================ random products
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("n,k,batch", [(37, 1024, 1), (300, 4096, 1), (129, 2304, 4),
+                                       (64, 256, 8), (70, 512, 64)])
+def test_gemv_random(wtype, n, k, batch):
+    print(f"gemv {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
+    rng = np.random.default_rng(31 * wtype + n + batch)
+    w = _special_rows(rng, n, k)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    y = qblk.qblk_gemv(wtype, dev_pack(wtype, w), n, k, dev_quantize(x), batch)
+    check_rel(host(y), expected(wtype, w, x))
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("m,n,k", [(1, 37, 256), (5, 300, 1024), (70, 129, 2304),
+                                   (130, 257, 512), (256, 128, 4096)])
+def test_gemm_random(wtype, m, n, k):
+    print(f"gemm {TNAME[wtype]} m={m} n={n} k={k}", flush=True)
+    rng = np.random.default_rng(41 * wtype + m + n)
+    w = _special_rows(rng, n, k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    y = qblk.qblk_gemm(wtype, dev_pack(wtype, w), n, k, dev_quantize(x), m)
+    check_rel(host(y), expected(wtype, w, x))
+
+
+def test_gemv_ldy_and_empty_calls():
+    print("gemv ldy / empty", flush=True)
+    rng = np.random.default_rng(5)
+    n, k, b = 100, 512, 3
+    w = _special_rows(rng, n, k)
+    x = rng.standard_normal((b, k)).astype(np.float32)
+    wq, xq = dev_pack(o.TYPE_Q4_K, w), dev_quantize(x)
+    ybig = torch().full((b, 160), -7.0, device="cuda")
+    qblk.qblk_gemv(o.TYPE_Q4_K, wq, n, k, xq, b, y=ybig[:, :n])
+    yh = host(ybig)
+    check_rel(yh[:, :n], expected(o.TYPE_Q4_K, w, x))
+    assert np.all(yh[:, n:] == -7.0)
+    # empty calls write nothing
+    qblk.qblk_gemv(o.TYPE_Q4_K, wq, 0, k, xq, b, y=ybig[:, :0])
+    qblk.qblk_gemm(o.TYPE_Q4_K, wq, 0, k, xq, b, y=ybig[:, :0])
+    assert np.all(host(ybig)[:, n:] == -7.0)
+
+
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+def test_deterministic(fn):
+    print(f"determinism {fn}", flush=True)
+    rng = np.random.default_rng(77)
+    n, k, m = 513, 4096, 4
+    w = _special_rows(rng, n, k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    wq, xq = dev_pack(o.TYPE_Q4_K, w), dev_quantize(x)
+    f = qblk.qblk_gemv if fn == "gemv" else qblk.qblk_gemm
+    a = host(f(o.TYPE_Q4_K, wq, n, k, xq, m))
+    b = host(f(o.TYPE_Q4_K, wq, n, k, xq, m))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ================================================================ full workload sizes
+
+def _sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(n, size=min(count, n), replace=False))
+    return np.unique(np.concatenate([[0, n - 1], rows]))
+
+
+def _full_size_check(wtype, w_dev, x_np, rows, use_gemm=False):
+    """Device: pack all of W, quantize x, product. Oracle: the sampled rows."""
+    n, k = w_dev.shape
+    m = x_np.shape[0]
+    wq = qblk.qblk_pack_weights(wtype, w_dev)
+    xq = dev_quantize(x_np)
+    f = qblk.qblk_gemm if use_gemm else qblk.qblk_gemv
+    y = host(f(wtype, wq, n, k, xq, m))
+    w_rows = host(w_dev[torch().from_numpy(rows).cuda()])
+    # the packed rows themselves are bit-exact
+    packed = host(wq).reshape(n, -1)[rows]
+    ref_packed, _ = o.encode_weights(wtype, w_rows)
+    assert np.array_equal(packed, ref_packed)
+    return check_rel(y[:, rows], expected(wtype, w_rows, x_np))
+
+
+@pytest.mark.parametrize("case", [
+    ("Q4_0 4096x4096", 1, o.TYPE_Q4_0, 4096, 4096),
+    ("Q8_0 14336x4096", 2, o.TYPE_Q8_0, 14336, 4096),
+    ("Q4_K q 4096x4096", 3, o.TYPE_Q4_K, 4096, 4096),
+    ("Q4_K k 1024x4096", 3, o.TYPE_Q4_K, 1024, 4096),
+    ("Q4_K gate 14336x4096", 3, o.TYPE_Q4_K, 14336, 4096),
+    ("Q4_K down 4096x14336", 3, o.TYPE_Q4_K, 4096, 14336),
+])
+def test_gemv_full_size_sampled(case):
+    name, wl, wtype, n, k = case
+    print(f"full-size gemv {name}", flush=True)
+    w = synth.weights(wl, 0, n, k)
+    x = synth.act(wl, 1, k)
+    _full_size_check(wtype, dev(w), x, _sample_rows(n, 96, n + k))
+
+
+@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("name,n,k", [("q", 8192, 8192), ("gate", 28672, 8192),
+                                      ("down", 8192, 28672)])
+def test_gemv_70b_layer_sampled(name, n, k, m):
+    print(f"70B-shaped gemv {name} {n}x{k} batch={m}", flush=True)
+    w = synth.torch_weights("student_t", 5000 + n % 97, n, k)
+    x = synth.act(5, m, k)
+    _full_size_check(o.TYPE_Q4_K, w, x, _sample_rows(n, 48, n))
+    del w
+    torch().cuda.empty_cache()
+
+
+@pytest.mark.parametrize("m", [512, 1, 8, 64])
+def test_gemm_prefill_full_size_sampled(m):
+    print(f"full-size gemm Q4_K m={m}", flush=True)
+    n, k = 14336, 4096
+    w = synth.weights(4, 0, n, k)
+    x = synth.act(4, m, k)
+    _full_size_check(o.TYPE_Q4_K, dev(w), x, _sample_rows(n, 64, m), use_gemm=True)
+    if m <= 64:   # the decode kernel on the same inputs agrees too
+        _full_size_check(o.TYPE_Q4_K, dev(w), x, _sample_rows(n, 32, m + 1))
