@@ -1,19 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the block-quantized product on one MI355X.
 
-Step = one decode pass over a 7B-shaped decoder layer with Q4_K weights
-(q, k, v, o 4096-wide, gate/up 14336x4096, down 4096x14336), batch 1: four
-activation quantizations and seven GEMVs. Weights are rotated over enough
-distinct packed copies of the layer that the 256 MB last-level cache cannot
-hold them, so every step streams its weights from HBM.
+Step = one decode token of a 70B-shaped model with Q4_K weights: 80 layers,
+each q/k/v (8192/1024/1024 x 8192), o (8192 x 8192), gate/up (28672 x 8192)
+and down (8192 x 28672) - one full 38.5 GB weight stream per token. q/k/v
+share an input and are packed as one 10240-row matrix, gate/up as one
+57344-row matrix (rows are independent in the packed layout, so this changes
+only the launch count). Per layer: four activation quantizations and four
+GEMVs, captured in a HIP graph per token.
 
-Headline value: effective packed-weight GB/s = weight bytes per step / step
-time. Also reported: the GEMV kernel's roofline fraction (HIP events around
-every launch), the prefill GEMM (512 x 14336 x 4096, int8 TOPS), the
-decode-vs-prefill crossover at M in {1, 8, 64}, and the CPU oracle on a bounded
-sample of the same workload.
+Headline value: effective packed-weight GB/s = weight bytes per token / time
+per token (batch 1). Also reported: batch 4, the GEMV kernel's roofline
+fraction from HIP events around every launch, a 7B-shaped layer with rotated
+weight copies, the prefill GEMM (512 x 14336 x 4096, int8 TOPS) with the
+decode/prefill crossover at M in {1, 8, 64}, the Q4_0 and Q8_0 GEMVs, and the
+CPU oracle on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--copies R] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--layers L] [--no-cpu-baseline]
 """
 
 import argparse
@@ -21,8 +24,6 @@ import json
 import os
 import sys
 import time
-
-import numpy as np
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 matrix-core peak, TOP/s
@@ -35,21 +36,152 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=30, help="timed decode tokens")
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=80)
     p.add_argument("--copies", type=int, default=8,
-                   help="distinct packed copies of the layer rotated through")
+                   help="distinct copies of the 7B-shaped layer rotated through")
     p.add_argument("--gemm-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
+
+
+# ---------------------------------------------------------------- timing helpers
+
+_SLEEP_CYCLES_PER_S = None
+
+
+def device_sleep(torch, seconds):
+    """Keep the GPU busy for about `seconds` so that work queued meanwhile
+    runs back to back (host launch latency stays outside event brackets)."""
+    global _SLEEP_CYCLES_PER_S
+    if _SLEEP_CYCLES_PER_S is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(10_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_S = 10_000_000 / (a.elapsed_time(b) * 1e-3)
+    torch.cuda._sleep(int(seconds * _SLEEP_CYCLES_PER_S))
+
+
+def time_replays(torch, graphs, steps, warmup):
+    for s in range(warmup):
+        graphs[s % len(graphs)].replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(steps):
+        graphs[s % len(graphs)].replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+# ---------------------------------------------------------------- decode model
+
+class DecodeModel:
+    """Packed Q4_K weights of `layers` layers and the per-layer launches of one
+    decode token: (quantize input, GEMV) for qkv, o, gate_up and down."""
+
+    def __init__(self, torch, qblk, synth, shapes, layers, seed0, dist, batch, dev):
+        self.torch, self.qblk = torch, qblk
+        self.batch = batch
+        groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]),
+                  ("down", ["down"])]
+        dims = {name: (n, k) for name, n, k in shapes}
+        self.groups = []
+        for gname, parts in groups:
+            k = dims[parts[0]][1]
+            n = sum(dims[p][0] for p in parts)
+            self.groups.append((gname, parts, n, k))
+        Q4_K = qblk.Q4_K
+        self.layers = []
+        for layer in range(layers):
+            packed = {}
+            for gname, parts, n, k in self.groups:
+                rb = qblk.qblk_weight_row_bytes(Q4_K, k)
+                buf = torch.empty(n * rb, dtype=torch.uint8, device=dev)
+                row = 0
+                for p in parts:
+                    pn = dims[p][0]
+                    idx = [s[0] for s in shapes].index(p)
+                    w = synth.torch_weights(dist, seed0 + 10 * layer + idx, pn, k, device=dev)
+                    qblk.qblk_pack_weights(Q4_K, w, out=buf[row * rb:(row + pn) * rb])
+                    del w
+                    row += pn
+                packed[gname] = buf
+            self.layers.append(packed)
+        torch.cuda.synchronize()
+        self.x = {g: synth.torch_activations(seed0 + 900 + i, batch, k, device=dev)
+                  for i, (g, _, _, k) in enumerate(self.groups)}
+        self.xq = {g: torch.empty(qblk.qblk_act_bytes(batch, k), dtype=torch.uint8, device=dev)
+                   for g, _, _, k in self.groups}
+        self.y = {g: torch.empty((batch, n), dtype=torch.float32, device=dev)
+                  for g, _, n, _ in self.groups}
+        self.weight_bytes = sum(qblk.qblk_weight_bytes(Q4_K, n, k)
+                                for _, _, n, k in self.groups) * layers
+
+    def token(self, events=None, layers=None):
+        qblk = self.qblk
+        for li, packed in enumerate(self.layers if layers is None else layers):
+            for g, _, n, k in self.groups:
+                qblk.qblk_quantize_act(self.x[g], out=self.xq[g])
+                if events is not None:
+                    events.append((g, n, k, self.torch.cuda.Event(enable_timing=True),
+                                   self.torch.cuda.Event(enable_timing=True)))
+                    events[-1][3].record()
+                qblk.qblk_gemv(qblk.Q4_K, packed[g], n, k, self.xq[g], self.batch, y=self.y[g])
+                if events is not None:
+                    events[-1][4].record()
+
+    def capture(self, layers=None):
+        torch = self.torch
+        self.token(layers=layers)
+        torch.cuda.synchronize()
+        eager = {g: y.clone() for g, y in self.y.items()}
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.token(layers=layers)
+        graph.replay()
+        torch.cuda.synchronize()
+        for g, y in self.y.items():
+            if not torch.equal(y, eager[g]):
+                raise RuntimeError(f"graph replay differs from the eager run ({g})")
+        return graph
+
+    def kernel_times(self, layers):
+        """HIP events around every GEMV launch of `layers` layers, queued
+        behind a device sleep. Returns (alg bytes, seconds, per-group)."""
+        torch, qblk = self.torch, self.qblk
+        events = []
+        device_sleep(torch, 0.02 + 4e-4 * len(layers) * len(self.groups))
+        self.token(events=events, layers=layers)
+        torch.cuda.synchronize()
+        per, tot_b, tot_s = {}, 0, 0.0
+        for g, n, k, a, b in events:
+            sec = a.elapsed_time(b) * 1e-3
+            alg = (qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + qblk.qblk_act_bytes(self.batch, k)
+                   + 4 * n * self.batch)
+            e = per.setdefault(g, {"n": n, "k": k, "launches": 0, "s": 0.0, "bytes": 0})
+            e["launches"] += 1
+            e["s"] += sec
+            e["bytes"] += alg
+            tot_b += alg
+            tot_s += sec
+        out = {g: {"n": e["n"], "k": e["k"], "us": round(1e6 * e["s"] / e["launches"], 3),
+                   "GBps": round(e["bytes"] / e["s"] / 1e9, 1)} for g, e in per.items()}
+        return tot_b, tot_s, out
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the product "
-                                   "shards by output rows, see the design notes",
+                                   "shards by weight rows across GPUs (see the design notes)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
@@ -57,99 +189,41 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    Q4_K = qblk.Q4_K
-    layer = synth.LAYER_7B
-    R = args.copies
 
-    # ------------------------------------------------------------ setup (untimed)
-    log(f"packing {R} copies of the 7B layer ({len(layer)} Q4_K linears)")
+    # ------------------------------------------------------------ 70B decode, batch 1 and 4
     t0 = time.time()
-    copies = []
-    for c in range(R):
-        packed = {}
-        for idx, (name, n, k) in enumerate(layer):
-            w = synth.torch_weights("outliers", 3000 + 100 * c + idx, n, k, device=dev)
-            packed[name] = qblk.qblk_pack_weights(Q4_K, w)
-            del w
-        copies.append(packed)
-    torch.cuda.synchronize()
-    log(f"packed in {time.time() - t0:.1f}s")
-    weight_bytes = sum(qblk.qblk_weight_bytes(Q4_K, n, k) for _, n, k in layer)
+    log(f"packing {args.layers} 70B-shaped Q4_K layers (Student-t weights)")
+    m1 = DecodeModel(torch, qblk, synth, synth.LAYER_70B, args.layers, 5000, "student_t", 1, dev)
+    log(f"packed {m1.weight_bytes / 1e9:.2f} GB in {time.time() - t0:.1f}s")
+    g1 = m1.capture()
+    ms_tok = time_replays(torch, [g1], args.steps, args.warmup)
+    value = m1.weight_bytes / (ms_tok * 1e-3) / 1e9
+    log(f"batch 1: {ms_tok:.3f} ms/token, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% "
+        f"of HBM peak)")
+    tot_b, tot_s, per_group = m1.kernel_times(m1.layers[:8])
+    achieved = tot_b / tot_s / 1e9
+    log(f"gemv kernel (events): {achieved:.1f} GB/s; {per_group}")
+    del g1
 
-    # activations: attention input (q,k,v), attention output (o), MLP input
-    # (gate, up), MLP hidden (down)
-    acts = {
-        "attn": synth.torch_activations(3099, 1, 4096, device=dev),
-        "o": synth.torch_activations(3098, 1, 4096, device=dev),
-        "mlp": synth.torch_activations(3097, 1, 4096, device=dev),
-        "down": synth.torch_activations(3096, 1, 14336, device=dev),
-    }
-    xq = {key: torch.empty(qblk.qblk_act_bytes(1, v.shape[1]), dtype=torch.uint8, device=dev)
-          for key, v in acts.items()}
-    src = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp",
-           "down": "down"}
-    ys = {name: torch.empty((1, n), dtype=torch.float32, device=dev) for name, n, _ in layer}
-
-    def step(s, events=None):
-        packed = copies[s % R]
-        qblk.qblk_quantize_act(acts["attn"], out=xq["attn"])
-        for name, n, k in layer:
-            if name == "o":
-                qblk.qblk_quantize_act(acts["o"], out=xq["o"])
-            elif name == "gate":
-                qblk.qblk_quantize_act(acts["mlp"], out=xq["mlp"])
-            elif name == "down":
-                qblk.qblk_quantize_act(acts["down"], out=xq["down"])
-            if events is not None:
-                events[name][0].record()
-            qblk.qblk_gemv(Q4_K, packed[name], n, k, xq[src[name]], 1, y=ys[name])
-            if events is not None:
-                events[name][1].record()
-
-    # ------------------------------------------------------------ timed: steps
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for s in range(args.steps):
-        step(s)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-    value = weight_bytes / (ms_step * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.2f} us, {value:.1f} GB/s effective weight bandwidth")
-
-    # ------------------------------------------------------------ timed: per-launch events
-    K_EV = min(args.steps, 100)
-    dur = {name: 0.0 for name, _, _ in layer}
-    for s in range(K_EV):
-        ev = {name: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for name, _, _ in layer}
-        step(s, ev)
-        torch.cuda.synchronize()
-        for name in dur:
-            dur[name] += ev[name][0].elapsed_time(ev[name][1])
-    per_launch = {}
-    alg_bytes_total = 0
-    dur_total_ms = 0.0
-    for name, n, k in layer:
-        alg = qblk.qblk_weight_bytes(Q4_K, n, k) + qblk.qblk_act_bytes(1, k) + 4 * n
-        d_ms = dur[name] / K_EV
-        per_launch[name] = {"n": n, "k": k, "us": round(d_ms * 1e3, 3),
-                            "GBps": round(alg / (d_ms * 1e-3) / 1e9, 1)}
-        alg_bytes_total += alg
-        dur_total_ms += d_ms
-    achieved = alg_bytes_total / (dur_total_ms * 1e-3) / 1e9
-    log(f"gemv kernel: {achieved:.1f} GB/s over {dur_total_ms * 1e3:.2f} us per layer")
-
-    del copies
+    m4 = m1
+    m4.batch = 4
+    m4.x = {g: synth.torch_activations(5950 + i, 4, k, device=dev)
+            for i, (g, _, _, k) in enumerate(m4.groups)}
+    m4.xq = {g: torch.empty(qblk.qblk_act_bytes(4, k), dtype=torch.uint8, device=dev)
+             for g, _, _, k in m4.groups}
+    m4.y = {g: torch.empty((4, n), dtype=torch.float32, device=dev) for g, _, n, _ in m4.groups}
+    g4 = m4.capture()
+    ms_tok4 = time_replays(torch, [g4], max(5, args.steps // 3), 1)
+    log(f"batch 4: {ms_tok4:.3f} ms/step, {m4.weight_bytes / (ms_tok4 * 1e-3) / 1e9:.1f} GB/s")
+    del g4, m1, m4
     torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ prefill GEMM
-    gemm = gemm_bench(torch, qblk, synth, dev, args.gemm_iters)
+    secondary = {}
+    if not args.no_secondary:
+        secondary["layer_7b"] = layer_7b(torch, qblk, synth, dev, args)
+        secondary["gemm"] = gemm_bench(torch, qblk, synth, dev, args.gemm_iters)
+        secondary["q4_0_q8_0"] = sym_bench(torch, qblk, synth, dev)
 
-    # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(synth, args.cpu_seconds)
@@ -161,34 +235,79 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 6),
+        "ms_per_step": round(ms_tok, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "q4_k_gemv_7b_layer",
-            "linears": {name: [n, k] for name, n, k in layer},
+            "workload": "q4_k_gemv_70b_decode_80_layers",
+            "layers": args.layers,
             "batch": 1,
-            "weight_bytes_per_step": weight_bytes,
-            "rotating_copies": R,
+            "weight_bytes_per_step": m_bytes(qblk, synth, args.layers),
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "tokens_per_s": round(1e3 / ms_tok, 2),
+            "batch4_ms_per_step": round(ms_tok4, 6),
+            "batch4_GBps": round(m_bytes(qblk, synth, args.layers) / (ms_tok4 * 1e-3) / 1e9, 2),
+            "launches_per_token": 8 * args.layers,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel<Q4_K,1>",
+            "kernel": "gemv_kernel<Q4_K, batch 1>",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "per_launch": per_launch,
+            "per_launch": per_group,
         },
-        "gemm": gemm,
+        "secondary": secondary,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def m_bytes(qblk, synth, layers):
+    return layers * sum(qblk.qblk_weight_bytes(qblk.Q4_K, n, k) for _, n, k in synth.LAYER_70B)
+
+
+def layer_7b(torch, qblk, synth, dev, args):
+    """One 7B-shaped layer, batch 1, weights rotated over `copies` distinct
+    packed copies (> 2 x the 256 MB last-level cache)."""
+    models = [DecodeModel(torch, qblk, synth, synth.LAYER_7B, 1, 3000 + 100 * c, "outliers", 1, dev)
+              for c in range(args.copies)]
+    graphs = [m.capture() for m in models]
+    ms = time_replays(torch, graphs, 200, 20)
+    wb = models[0].weight_bytes
+    tot_b, tot_s, per = 0, 0.0, {}
+    for m in models[:4]:
+        b, s, per = m.kernel_times(m.layers)
+        tot_b += b
+        tot_s += s
+    res = {"workload": "q4_k_gemv_7b_layer", "us_per_layer": round(ms * 1e3, 3),
+           "GBps": round(wb / (ms * 1e-3) / 1e9, 1), "weight_bytes": wb,
+           "kernel_GBps": round(tot_b / tot_s / 1e9, 1), "per_launch": per,
+           "rotating_copies": args.copies}
+    log(f"7B layer: {res}")
+    del graphs, models
+    torch.cuda.empty_cache()
+    return res
+
+
+def timed_launches(torch, fn, iters):
+    for _ in range(3):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    device_sleep(torch, 0.01 + 3e-4 * iters)
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return 1e3 * sum(a.elapsed_time(b) for a, b in ev) / iters   # us
 
 
 def gemm_bench(torch, qblk, synth, dev, iters):
@@ -209,17 +328,7 @@ def gemm_bench(torch, qblk, synth, dev, iters):
         if m <= 64:
             fns.append(("gemv", qblk.qblk_gemv))
         for fname, f in fns:
-            for _ in range(5):
-                f(Q4_K, wq, n, k, xq, m, y=y)
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(iters)]
-            for a, b in ev:
-                a.record()
-                f(Q4_K, wq, n, k, xq, m, y=y)
-                b.record()
-            torch.cuda.synchronize()
-            us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / iters
+            us = timed_launches(torch, lambda i: f(Q4_K, wq, n, k, xq, m, y=y), iters)
             ops = 2.0 * m * n * k
             row[fname] = {"us": round(us, 3), "TOPS": round(ops / (us * 1e-6) / 1e12, 2)}
         res[f"m{m}"] = row
@@ -236,19 +345,43 @@ def gemm_bench(torch, qblk, synth, dev, iters):
     }
 
 
+def sym_bench(torch, qblk, synth, dev):
+    """Q4_0 4096 x 4096 and Q8_0 14336 x 4096 GEMVs, batch 1, rotated over
+    enough copies to exceed the last-level cache."""
+    res = {}
+    for name, t, n, k in (("q4_0_gemv_4096x4096", qblk.Q4_0, 4096, 4096),
+                          ("q8_0_gemv_14336x4096", qblk.Q8_0, 14336, 4096)):
+        wb = qblk.qblk_weight_bytes(t, n, k)
+        copies = max(2, int(600e6 // wb) + 1)
+        wqs = []
+        for c in range(copies):
+            w = synth.torch_weights("normal", 1000 * t + c, n, k, device=dev)
+            wqs.append(qblk.qblk_pack_weights(t, w))
+            del w
+        xq = qblk.qblk_quantize_act(synth.torch_activations(1000 * t + 99, 1, k, device=dev))
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        us = timed_launches(torch, lambda i: qblk.qblk_gemv(t, wqs[i % copies], n, k, xq, 1, y=y),
+                            100)
+        res[name] = {"us": round(us, 3), "weight_bytes": wb, "GBps": round(wb / (us * 1e-6) / 1e9, 1)}
+        log(f"{name}: {res[name]}")
+        del wqs
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(synth, seconds):
-    """The oracle (NumPy, int64 block sums + fp64 scaling) on the host cores,
-    over a bounded sample of the same layer: the first 256 rows of each of
-    the seven linears, encoded untimed, then activation quantization plus the
-    product timed, repeated until `seconds` have elapsed."""
+    """The oracle (NumPy: int64 block sums, fp64 scaling) on the host cores,
+    over a bounded sample of the headline workload: the first 32 rows of each
+    of the seven 70B-shaped Q4_K linears (encoded untimed), then activation
+    quantization plus the product timed, repeated until `seconds` elapse."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from oracle import qblk_oracle as o
-    rows = 256
+    rows = 32
     samples = []
-    for idx, (name, n, k) in enumerate(synth.LAYER_7B):
-        w = synth.weights_outliers(3900 + idx, rows, k)
+    for idx, (name, n, k) in enumerate(synth.LAYER_70B):
+        w = synth.weights_student_t(5900 + idx, rows, k)
         _, enc = o.encode_weights(o.TYPE_Q4_K, w)
-        x = synth.activations(3999 - idx, 1, k)
+        x = synth.activations(5999 - idx, 1, k)
         samples.append((enc, x, o.row_bytes(o.TYPE_Q4_K, k) * rows))
     done_bytes = 0
     t0 = time.perf_counter()
@@ -265,10 +398,10 @@ def cpu_baseline(synth, seconds):
     gbs = done_bytes / el / 1e9
     log(f"cpu oracle: {gbs:.4f} GB/s over {el:.1f}s")
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} rows of each of the 7 Q4_K linears of the 7B layer, "
-                      f"batch 1, {reps} passes in {el:.1f}s (activation quantization + "
-                      f"int64 block sums + fp64 scaling; weight encoding untimed); NumPy "
-                      f"int64 einsum runs on one thread",
+            "sample": f"first {rows} rows of each of the 7 Q4_K linears of a 70B-shaped layer, "
+                      f"batch 1, {reps} passes in {el:.1f}s (activation quantization + int64 "
+                      f"block sums + fp64 scaling; weight encoding untimed); NumPy's int64 "
+                      f"einsum runs on one thread",
             "host_cores": len(os.sched_getaffinity(0))}
 
 

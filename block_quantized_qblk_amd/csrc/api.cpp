@@ -14,8 +14,11 @@ thread_local int g_last_hip_error = 0;
 
 bool valid_type(int t) { return t == QBLK_Q4_0 || t == QBLK_Q8_0 || t == QBLK_Q4_K; }
 
+// Largest k accepted: row offsets inside the kernels are 32-bit.
+constexpr int64_t kMaxK = int64_t{1} << 28;
+
 bool valid_k(int t, int64_t k) {
-  if (k <= 0) return false;
+  if (k <= 0 || k > kMaxK) return false;
   return t == QBLK_Q4_K ? (k % 256 == 0) : (k % 32 == 0);
 }
 

@@ -87,6 +87,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// DPP move of v; lanes of rows disabled by ROW_MASK read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes with DPP only; the total lands in lane 63.
+//   quad_perm(1,0,3,2), quad_perm(2,3,0,1): sums of 4 lanes
+//   row_half_mirror, row_mirror: sums of 8, then 16 lanes (one row)
+//   row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_move<0xB1, 0xF>(v);
+  v += dpp_move<0x4E, 0xF>(v);
+  v += dpp_move<0x141, 0xF>(v);
+  v += dpp_move<0x140, 0xF>(v);
+  v += dpp_move<0x142, 0xA>(v);
+  v += dpp_move<0x143, 0xC>(v);
+  return v;
+}
+
 // Activation buffer views (m rows of k): codes, then (d, sum) pairs.
 struct ActView {
   const uint8_t* q;   // [m][k] int8 codes
