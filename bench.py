@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="only run a 1 GiB device copy and the GEMVs of 4 layers once "
+                        "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
     return p.parse_args()
 
 
@@ -125,16 +128,34 @@ class DecodeModel:
         self.weight_bytes = sum(qblk.qblk_weight_bytes(Q4_K, n, k)
                                 for _, _, n, k in self.groups) * layers
 
+    # the fused entry point repeats the quantization in every workgroup: it
+    # beats quantize + GEMV (one kernel boundary more) only on small matrices
+    FUSED_MAX_ELEMS = 32 << 20
+
+    def fused(self, k, n=None):
+        n = n if n is not None else max(gn for _, _, gn, gk in self.groups if gk == k)
+        return (n * k <= self.FUSED_MAX_ELEMS
+                and self.batch <= self.qblk.qblk_gemv_f32_max_batch(k))
+
     def token(self, events=None, layers=None):
+        """One decode token: per layer and group, the activation quantization
+        fused into the GEMV when its codes fit local memory, else
+        qblk_quantize_act followed by qblk_gemv."""
         qblk = self.qblk
         for li, packed in enumerate(self.layers if layers is None else layers):
             for g, _, n, k in self.groups:
-                qblk.qblk_quantize_act(self.x[g], out=self.xq[g])
+                fused = self.fused(k, n)
+                if not fused:
+                    qblk.qblk_quantize_act(self.x[g], out=self.xq[g])
                 if events is not None:
                     events.append((g, n, k, self.torch.cuda.Event(enable_timing=True),
                                    self.torch.cuda.Event(enable_timing=True)))
                     events[-1][3].record()
-                qblk.qblk_gemv(qblk.Q4_K, packed[g], n, k, self.xq[g], self.batch, y=self.y[g])
+                if fused:
+                    qblk.qblk_gemv_f32(qblk.Q4_K, packed[g], n, k, self.x[g], y=self.y[g])
+                else:
+                    qblk.qblk_gemv(qblk.Q4_K, packed[g], n, k, self.xq[g], self.batch,
+                                   y=self.y[g])
                 if events is not None:
                     events[-1][4].record()
 
@@ -164,8 +185,8 @@ class DecodeModel:
         per, tot_b, tot_s = {}, 0, 0.0
         for g, n, k, a, b in events:
             sec = a.elapsed_time(b) * 1e-3
-            alg = (qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + qblk.qblk_act_bytes(self.batch, k)
-                   + 4 * n * self.batch)
+            act = 4 * k * self.batch if self.fused(k, n) else qblk.qblk_act_bytes(self.batch, k)
+            alg = qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + act + 4 * n * self.batch
             e = per.setdefault(g, {"n": n, "k": k, "launches": 0, "s": 0.0, "bytes": 0})
             e["launches"] += 1
             e["s"] += sec
@@ -189,6 +210,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.traffic_probe:
+        traffic_probe(torch, qblk, synth, dev)
+        return
 
     # ------------------------------------------------------------ 70B decode, batch 1 and 4
     t0 = time.time()
@@ -251,6 +275,9 @@ def main():
             "batch4_ms_per_step": round(ms_tok4, 6),
             "batch4_GBps": round(m_bytes(qblk, synth, args.layers) / (ms_tok4 * 1e-3) / 1e9, 2),
             "launches_per_token": 8 * args.layers,
+            "activation_quantization": "qblk_quantize_act before each GEMV (the fused "
+                                       "qblk_gemv_f32 is used only for matrices of at most "
+                                       "32M weights, where it is faster)",
         },
         "roofline": {
             "bound": "hbm",
@@ -259,13 +286,66 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic_from_profile(),
             "per_launch": per_group,
         },
         "secondary": secondary,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------- HBM traffic
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_q4k_70b_decode_traffic.md")
+KERNEL_SOURCES = ["block_quantized_qblk_amd/csrc/gemv.hip",
+                  "block_quantized_qblk_amd/csrc/qblk_device.h"]
+
+
+def kernel_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile():
+    """Measured HBM bytes per GEMV launch from the committed counter summary,
+    or None when it is missing or was taken on different kernel sources."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    import re
+    m = re.search(r"<!-- traffic (\{.*?\}) -->", text)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_sha256") != kernel_sha256():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def traffic_probe(torch, qblk, synth, dev):
+    """Calibration copy of 1 GiB, then the four GEMVs of four 70B-shaped
+    layers once (batch 1). Prints the algorithmic bytes of each GEMV launch."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    m = DecodeModel(torch, qblk, synth, synth.LAYER_70B, 4, 5000, "student_t", 1, dev)
+    m.token()
+    torch.cuda.synchronize()
+    alg = [{"group": g, "n": n, "k": k,
+            "alg_bytes": qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + 4 * k + 4 * n}
+           for _ in range(4) for g, _, n, k in m.groups]
+    print(json.dumps({"copy_bytes_each_way": 1 << 30, "gemv_launches": alg,
+                      "kernel_sha256": kernel_sha256()}))
 
 
 def m_bytes(qblk, synth, layers):

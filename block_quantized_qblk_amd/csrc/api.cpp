@@ -117,6 +117,24 @@ QBLK_EXPORT int qblk_gemv(int type, const void* wq, int64_t n, int64_t k, const 
   return finish(qblk::launch_gemv(type, wq, n, k, xq, batch, y, ldy, stream));
 }
 
+QBLK_EXPORT int qblk_gemv_f32_max_batch(int64_t k) {
+  if (k <= 0 || k % 32 != 0 || k > kMaxK) return 0;
+  return static_cast<int>(qblk::gemv_f32_max_batch(k));
+}
+
+QBLK_EXPORT int qblk_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
+                              int64_t ldx, int64_t batch, float* y, int64_t ldy,
+                              hipStream_t stream) {
+  const int st = check_product(type, wq, n, k, x, batch, y, ldy);
+  if (st != QBLK_OK || n == 0 || batch == 0) return st;
+  if (ldx < k) return QBLK_ERR_SHAPE;
+  if (!aligned(x, 16) || ldx % 4 != 0) return QBLK_ERR_ALIGN;
+  if (batch > qblk::gemv_f32_max_batch(k)) return QBLK_ERR_UNSUPPORTED;
+  if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, stream));
+}
+
 QBLK_EXPORT int qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                           int64_t m, float* y, int64_t ldy, hipStream_t stream) {
   const int st = check_product(type, wq, n, k, xq, m, y, ldy);

@@ -108,6 +108,63 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------- Q8 activation quantizer
+// One 32-block is quantized by four consecutive lanes, 8 elements each
+// ("llama.cpp 推理引擎", §5.1 at b = 8): d = max|x| / 127 and q = round(x / d),
+// both IEEE fp32 divisions (correctly rounded), round half away from zero,
+// d == 0 gives q == 0. Returns the lane's 8 codes packed in the element order
+// 0,2,4,6 | 1,3,5,7; the block's scale and code sum come back in d / sum
+// (valid in every lane of the group). The group is an aligned quad of lanes
+// (lanes 4i..4i+3) and all four must be active.
+struct Q8Group {
+  uint2 codes;
+  float d;
+  int sum;
+};
+
+// Value of lane (l ^ 1) / (l ^ 2) within each aligned quad of lanes (DPP
+// quad_perm), for the 4-lane groups of the quantizer.
+template <int CTRL>
+__device__ __forceinline__ int quad_swap(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __builtin_bit_cast(float, quad_swap<CTRL>(__builtin_bit_cast(int, v)));
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+__device__ __forceinline__ Q8Group quantize_group8(const float (&e)[8]) {
+#pragma clang fp contract(off)
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(e[i]));
+  amax = fmaxf(amax, quad_swap<kQuadXor1>(amax));
+  amax = fmaxf(amax, quad_swap<kQuadXor2>(amax));
+  Q8Group r;
+  r.d = __fdiv_rn(amax, 127.0f);
+  int q[8];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int qi = 0;
+    if (r.d != 0.0f) {
+      float t = roundf(__fdiv_rn(e[i], r.d));  // half away from zero
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      qi = static_cast<int>(t);
+    }
+    q[i] = qi;
+    s += qi;
+  }
+  s += quad_swap<kQuadXor1>(s);
+  s += quad_swap<kQuadXor2>(s);
+  r.sum = s;
+  r.codes.x = (q[0] & 255u) | (q[2] & 255u) << 8 | (q[4] & 255u) << 16 | (q[6] & 255u) << 24;
+  r.codes.y = (q[1] & 255u) | (q[3] & 255u) << 8 | (q[5] & 255u) << 16 | (q[7] & 255u) << 24;
+  return r;
+}
+
 // Activation buffer views (m rows of k): codes, then (d, sum) pairs.
 struct ActView {
   const uint8_t* q;   // [m][k] int8 codes

@@ -40,6 +40,12 @@ hipError_t launch_pack_weights(int type, const float* w, int64_t n, int64_t k, i
                                void* wq, hipStream_t s);
 hipError_t launch_gemv(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t batch, float* y, int64_t ldy, hipStream_t s);
+// Fused quantize + GEMV (fp32 activations): up to 8 activation rows per
+// launch; the kernel keeps two 64-block slices of their codes in LDS
+// (5 KiB per row), so the limit does not depend on k.
+inline int64_t gemv_f32_max_batch(int64_t k) { return k > 0 ? 8 : 0; }
+hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
+                           int64_t ldx, int64_t batch, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t m, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,

@@ -14,14 +14,6 @@
 namespace qblk {
 namespace {
 
-// Pack 8 int8 codes as two dwords in the element order 0,2,4,6 | 1,3,5,7.
-__device__ __forceinline__ uint2 pack_group8(const int (&q)[8]) {
-  uint2 r;
-  r.x = (q[0] & 255u) | (q[2] & 255u) << 8 | (q[4] & 255u) << 16 | (q[6] & 255u) << 24;
-  r.y = (q[1] & 255u) | (q[3] & 255u) << 8 | (q[5] & 255u) << 16 | (q[7] & 255u) << 24;
-  return r;
-}
-
 // Four consecutive lanes handle one 32-block, 8 elements each.
 __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x, int64_t m,
                                                            int64_t k, int64_t ldx,
@@ -38,35 +30,13 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
   const float4 v0 = *reinterpret_cast<const float4*>(src);
   const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
   const float e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  const Q8Group r = quantize_group8(e);
 
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(e[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-
-  const float d = __fdiv_rn(amax, 127.0f);
-  int q[8];
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int qi = 0;
-    if (d != 0.0f) {
-      float r = roundf(__fdiv_rn(e[i], d));  // half away from zero
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      qi = static_cast<int>(r);
-    }
-    q[i] = qi;
-    s += qi;
-  }
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-
-  *reinterpret_cast<uint2*>(xq + row * k + 32 * blk + 8 * sub) = pack_group8(q);
+  *reinterpret_cast<uint2*>(xq + row * k + 32 * blk + 8 * sub) = r.codes;
   if (sub == 0) {
     float2 ds;
-    ds.x = d;
-    ds.y = __int_as_float(s);
+    ds.x = r.d;
+    ds.y = __int_as_float(r.sum);
     *reinterpret_cast<float2*>(xq + m * k + 8 * (row * nb + blk)) = ds;
   }
 }

@@ -46,6 +46,8 @@ def _load():
         "qblk_quantize_act": (i32, [vp, i64, i64, i64, vp, vp]),
         "qblk_gemv": (i32, [i32, vp, i64, i64, vp, i64, vp, i64, vp]),
         "qblk_gemm": (i32, [i32, vp, i64, i64, vp, i64, vp, i64, vp]),
+        "qblk_gemv_f32_max_batch": (i32, [i64]),
+        "qblk_gemv_f32": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]),
         "qblk_block_sums": (i32, [i32, vp, i64, i64, vp, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -173,6 +175,33 @@ def _product(fname, wtype, wq, n, k, xq, m, y, stream):
 def qblk_gemv(wtype, wq, n, k, xq, batch=1, y=None, stream=None):
     """y[b, :n] = W x_b for b < batch (decode path, batch <= 64)."""
     return _product("qblk_gemv", wtype, wq, n, k, xq, batch, y, stream)
+
+
+def qblk_gemv_f32_max_batch(k):
+    return int(_load().qblk_gemv_f32_max_batch(int(k)))
+
+
+def qblk_gemv_f32(wtype, wq, n, k, x, batch=None, y=None, stream=None):
+    """y[b, :n] = W quant(x_b): activation quantization fused into the GEMV.
+    x: float32 [batch, >= k] device tensor with unit stride along rows."""
+    import torch
+    _require_cuda(wq, "wq")
+    _require_cuda(x, "x", rows=True)
+    if x.dtype != torch.float32 or x.shape[1] < k:
+        raise ValueError("x must be float32 [batch, >= k]")
+    if batch is None:
+        batch = x.shape[0]
+    if y is None:
+        y = torch.empty((batch, n), dtype=torch.float32, device=wq.device)
+    _require_cuda(y, "y", rows=True)
+    if y.dtype != torch.float32 or y.shape[0] < batch or y.shape[1] < n:
+        raise ValueError("y must be float32 [batch, >= n]")
+    if wq.numel() < qblk_weight_bytes(wtype, n, k):
+        raise ValueError("wq smaller than the packed size")
+    _check(_load().qblk_gemv_f32(_type(wtype), _ptr(wq), int(n), int(k), _ptr(x), x.stride(0),
+                                 int(batch), _ptr(y), y.stride(0), _stream(stream)),
+           "qblk_gemv_f32")
+    return y
 
 
 def qblk_gemm(wtype, wq, n, k, xq, m, y=None, stream=None):

@@ -151,12 +151,31 @@ int qblk_quantize_act(const float *x, int64_t m, int64_t k, int64_t ldx,
  *   activation block sum. Accumulation is fp32 in an unspecified order.
  *   wq : packed weights [n] rows of k;  xq : activation buffer of `batch`
  *   rows of k (from qblk_quantize_act);  y : fp32 [batch][ldy].
- * Errors: QBLK_ERR_ARG, QBLK_ERR_SHAPE (k invalid, ldy < n when batch > 1),
+ * Errors: QBLK_ERR_ARG, QBLK_ERR_SHAPE (k invalid or above 2^28, ldy < n),
  * QBLK_ERR_ALIGN, QBLK_ERR_UNSUPPORTED (batch > QBLK_GEMV_MAX_BATCH),
  * QBLK_ERR_LAUNCH.
  */
 int qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void *xq,
               int64_t batch, float *y, int64_t ldy, hipStream_t stream);
+
+/*
+ * Decode-path product with the activation quantization fused in: the same
+ * result, bit for bit, as qblk_quantize_act(x) followed by qblk_gemv, but in
+ * one launch and without the activation buffer. Each workgroup quantizes
+ * the fp32 rows, 64 blocks at a time, into its local memory with the
+ * qblk_quantize_act rule ("llama.cpp 推理引擎", §5.1 at 8 bits) while it
+ * streams its weight rows. Every workgroup repeats the quantization, so this
+ * saves time over the two-step path only for small matrices (measured on
+ * MI355X: up to about 4096 x 4096).
+ *   x : fp32 [batch][ldx];  other arguments as qblk_gemv.
+ * batch <= qblk_gemv_f32_max_batch(k) (8 for any valid k, 0 when k is
+ * invalid).
+ * Errors: as qblk_gemv, plus QBLK_ERR_SHAPE for ldx < k, QBLK_ERR_ALIGN for x
+ * or ldx, QBLK_ERR_UNSUPPORTED for batch > qblk_gemv_f32_max_batch(k).
+ */
+int qblk_gemv_f32_max_batch(int64_t k);
+int qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const float *x,
+                  int64_t ldx, int64_t batch, float *y, int64_t ldy, hipStream_t stream);
 
 /*
  * Prefill-path product: the same result as qblk_gemv for m activation rows,

@@ -300,3 +300,49 @@ def test_gemm_prefill_full_size_sampled(m):
     _full_size_check(o.TYPE_Q4_K, dev(w), x, _sample_rows(n, 64, m), use_gemm=True)
     if m <= 64:   # the decode kernel on the same inputs agrees too
         _full_size_check(o.TYPE_Q4_K, dev(w), x, _sample_rows(n, 32, m + 1))
+
+
+# ================================================================ fused quantize + GEMV
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("n,k,batch", [(37, 1024, 1), (300, 4096, 3), (4100, 2304, 1),
+                                       (9000, 8192, 1), (129, 4096, 6), (70, 256, 8),
+                                       (2000, 28672, 1), (17000, 4096, 1), (8200, 16384, 1),
+                                       (5000, 28672, 4)])
+def test_gemv_f32_matches_quantize_then_gemv(wtype, n, k, batch):
+    if wtype == o.TYPE_Q4_K and k % 256:
+        pytest.skip("Q4_K needs k % 256 == 0")
+    print(f"gemv_f32 {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
+    assert batch <= qblk.qblk_gemv_f32_max_batch(k)
+    rng = np.random.default_rng(61 * wtype + n + batch)
+    w = _special_rows(rng, n, k)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    x[0, :32] = 0
+    wq = dev_pack(wtype, w)
+    xd = dev(x)
+    fused = host(qblk.qblk_gemv_f32(wtype, wq, n, k, xd))
+    two_step = host(qblk.qblk_gemv(wtype, wq, n, k, qblk.qblk_quantize_act(xd), batch))
+    assert np.array_equal(fused.view(np.uint32), two_step.view(np.uint32))
+    if n * k <= 2000 * 28672:
+        rows = _sample_rows(n, 64, n + batch)
+        check_rel(fused[:, rows], expected(wtype, w[rows], x))
+
+
+def test_gemv_f32_strided_rows_and_limits():
+    print("gemv_f32 strided x / limits", flush=True)
+    rng = np.random.default_rng(8)
+    n, k = 513, 2048
+    w = _special_rows(rng, n, k)
+    big = rng.standard_normal((3, k + 64)).astype(np.float32)
+    wq = dev_pack(o.TYPE_Q4_K, w)
+    xs = dev(big)[:, 32:32 + k]
+    y = host(qblk.qblk_gemv_f32(o.TYPE_Q4_K, wq, n, k, xs))
+    check_rel(y, expected(o.TYPE_Q4_K, w, big[:, 32:32 + k]))
+    assert qblk.qblk_gemv_f32_max_batch(28672) == 8
+    assert qblk.qblk_gemv_f32_max_batch(4096) == 8
+    assert qblk.qblk_gemv_f32_max_batch(100) == 0
+    x9 = dev(rng.standard_normal((9, 256)).astype(np.float32))
+    wq9 = dev_pack(o.TYPE_Q4_K, _special_rows(rng, 8, 256))
+    with pytest.raises(qblk.QblkError) as ei:
+        qblk.qblk_gemv_f32(o.TYPE_Q4_K, wq9, 8, 256, x9)
+    assert ei.value.status == -4
