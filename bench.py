@@ -11,7 +11,8 @@ GEMVs, captured in a HIP graph per token.
 
 Headline value: effective packed-weight GB/s = weight bytes per token / time
 per token (batch 1). Also reported: batch 4, the GEMV kernel's roofline
-fraction from HIP events around every launch, a 7B-shaped layer with rotated
+fraction (HIP-event-timed graphs of back-to-back GEMV launches, the same
+boundary-to-boundary time a kernel trace reports), a 7B-shaped layer with rotated
 weight copies, the prefill GEMM (512 x 14336 x 4096, int8 TOPS) with the
 decode/prefill crossover at M in {1, 8, 64}, the Q4_0 and Q8_0 GEMVs, and the
 CPU oracle on a bounded sample of the same workload.
@@ -137,7 +138,7 @@ class DecodeModel:
         return (n * k <= self.FUSED_MAX_ELEMS
                 and self.batch <= self.qblk.qblk_gemv_f32_max_batch(k))
 
-    def token(self, events=None, layers=None):
+    def token(self, layers=None):
         """One decode token: per layer and group, the activation quantization
         fused into the GEMV when its codes fit local memory, else
         qblk_quantize_act followed by qblk_gemv."""
@@ -147,17 +148,11 @@ class DecodeModel:
                 fused = self.fused(k, n)
                 if not fused:
                     qblk.qblk_quantize_act(self.x[g], out=self.xq[g])
-                if events is not None:
-                    events.append((g, n, k, self.torch.cuda.Event(enable_timing=True),
-                                   self.torch.cuda.Event(enable_timing=True)))
-                    events[-1][3].record()
                 if fused:
                     qblk.qblk_gemv_f32(qblk.Q4_K, packed[g], n, k, self.x[g], y=self.y[g])
                 else:
                     qblk.qblk_gemv(qblk.Q4_K, packed[g], n, k, self.xq[g], self.batch,
                                    y=self.y[g])
-                if events is not None:
-                    events[-1][4].record()
 
     def capture(self, layers=None):
         torch = self.torch
@@ -175,27 +170,39 @@ class DecodeModel:
         return graph
 
     def kernel_times(self, layers):
-        """HIP events around every GEMV launch of `layers` layers, queued
-        behind a device sleep. Returns (alg bytes, seconds, per-group)."""
+        """Per-launch GEMV time: for each group, one HIP graph of its GEMV over
+        `layers` layers back to back (the activation quantized once before),
+        bracketed by HIP events on the launch stream; time / launches is the
+        kernel's boundary-to-boundary duration, as a kernel trace reports it.
+        Returns (algorithmic bytes, seconds, per-group table)."""
         torch, qblk = self.torch, self.qblk
-        events = []
-        device_sleep(torch, 0.02 + 4e-4 * len(layers) * len(self.groups))
-        self.token(events=events, layers=layers)
-        torch.cuda.synchronize()
         per, tot_b, tot_s = {}, 0, 0.0
-        for g, n, k, a, b in events:
-            sec = a.elapsed_time(b) * 1e-3
-            act = 4 * k * self.batch if self.fused(k, n) else qblk.qblk_act_bytes(self.batch, k)
-            alg = qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + act + 4 * n * self.batch
-            e = per.setdefault(g, {"n": n, "k": k, "launches": 0, "s": 0.0, "bytes": 0})
-            e["launches"] += 1
-            e["s"] += sec
-            e["bytes"] += alg
+        for g, _, n, k in self.groups:
+            fused = self.fused(k, n)
+            if not fused:
+                qblk.qblk_quantize_act(self.x[g], out=self.xq[g])
+
+            def launches():
+                for packed in layers:
+                    if fused:
+                        qblk.qblk_gemv_f32(qblk.Q4_K, packed[g], n, k, self.x[g], y=self.y[g])
+                    else:
+                        qblk.qblk_gemv(qblk.Q4_K, packed[g], n, k, self.xq[g], self.batch,
+                                       y=self.y[g])
+            launches()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                launches()
+            sec = time_replays(torch, [graph], 3, 1) * 1e-3
+            del graph
+            act = 4 * k * self.batch if fused else qblk.qblk_act_bytes(self.batch, k)
+            alg = (qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + act + 4 * n * self.batch) * len(layers)
+            per[g] = {"n": n, "k": k, "us": round(1e6 * sec / len(layers), 3),
+                      "GBps": round(alg / sec / 1e9, 1), "fused_quantization": fused}
             tot_b += alg
             tot_s += sec
-        out = {g: {"n": e["n"], "k": e["k"], "us": round(1e6 * e["s"] / e["launches"], 3),
-                   "GBps": round(e["bytes"] / e["s"] / 1e9, 1)} for g, e in per.items()}
-        return tot_b, tot_s, out
+        return tot_b, tot_s, per
 
 
 def main():
@@ -224,9 +231,9 @@ def main():
     value = m1.weight_bytes / (ms_tok * 1e-3) / 1e9
     log(f"batch 1: {ms_tok:.3f} ms/token, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% "
         f"of HBM peak)")
-    tot_b, tot_s, per_group = m1.kernel_times(m1.layers[:8])
+    tot_b, tot_s, per_group = m1.kernel_times(m1.layers)
     achieved = tot_b / tot_s / 1e9
-    log(f"gemv kernel (events): {achieved:.1f} GB/s; {per_group}")
+    log(f"gemv kernel (graphs of back-to-back launches): {achieved:.1f} GB/s; {per_group}")
     del g1
 
     m4 = m1
@@ -342,7 +349,8 @@ def traffic_probe(torch, qblk, synth, dev):
     m.token()
     torch.cuda.synchronize()
     alg = [{"group": g, "n": n, "k": k,
-            "alg_bytes": qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + 4 * k + 4 * n}
+            "alg_bytes": qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + 4 * n
+            + (4 * k if m.fused(k, n) else qblk.qblk_act_bytes(1, k))}
            for _ in range(4) for g, _, n, k in m.groups]
     print(json.dumps({"copy_bytes_each_way": 1 << 30, "gemv_launches": alg,
                       "kernel_sha256": kernel_sha256()}))
@@ -360,11 +368,7 @@ def layer_7b(torch, qblk, synth, dev, args):
     graphs = [m.capture() for m in models]
     ms = time_replays(torch, graphs, 200, 20)
     wb = models[0].weight_bytes
-    tot_b, tot_s, per = 0, 0.0, {}
-    for m in models[:4]:
-        b, s, per = m.kernel_times(m.layers)
-        tot_b += b
-        tot_s += s
+    tot_b, tot_s, per = models[0].kernel_times([m.layers[0] for m in models])
     res = {"workload": "q4_k_gemv_7b_layer", "us_per_layer": round(ms * 1e3, 3),
            "GBps": round(wb / (ms * 1e-3) / 1e9, 1), "weight_bytes": wb,
            "kernel_GBps": round(tot_b / tot_s / 1e9, 1), "per_launch": per,

@@ -40,6 +40,12 @@ COMMON = [
 ]
 
 
+# per-source extra flags: the GEMM's MFMA results feed VALU instructions
+# directly, so MFMAs write VGPRs instead of accumulation registers (no copy
+# back per result)
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc():
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -49,7 +55,7 @@ def hipcc():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + EXTRA.get(src, [])
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -2,9 +2,32 @@
 //
 // Dequantize-free: each 32-block's integer dot product is one
 // v_mfma_i32_32x32x32_i8 over a 32x32 output tile (K = 32 is exactly one
-// block), and the block scales are applied to the int32 tile in fp32 right
+// block) and the block scales are applied to the int32 tile in fp32 right
 // after it ("llama.cpp 推理引擎", §6.4: scales outside the integer values;
-// §5.5 Q4_K sub-block scale and min; §7.3: prefill is compute-bound).
+// §5.5: Q4_K sub-block scale d*sc_j and min d_min*mn_j; §7.3: prefill is
+// compute-bound).
+//
+// Per (m, n, block) the scale step is the binding cost (the matrix core does
+// the 32x32x32 block in 32 cycles, the VALU needs 4 cycles per instruction
+// for the tile's 16 values per lane), so it is cut to two FMAs:
+//   * the int32 accumulator of each block MFMA starts from the bit pattern of
+//     the float 1.5 * 2^23, so the result, read as fp32, is 1.5 * 2^23 + S
+//     exactly (|S| < 2^22), and fma(F, sw, -1.5 * 2^23 * sw) = round(S * sw)
+//     in one instruction - exact for Q4_K, whose sw = d * sc_j has at most 17
+//     significant bits so that 1.5 * 2^23 * sw is an fp32 number;
+//   * acc = fma(S * sw, sa, acc) applies the activation scale.
+// The min terms (Q4_K: sum_b (sa*A)[m][b] * (d_min*mn_j)[n][b]; Q4_0, whose
+// codes are nibble - 8: sum_b (sa*A)[m][b] * (-8*d)[n][b]) are an fp32 matrix
+// product over blocks and run on the matrix cores (v_mfma_f32_32x32x2f32).
+// Q4_0 / Q8_0 scales are full fp32, so their main step converts S exactly
+// and takes three instructions.
+//
+// Data movement: K steps of 4 blocks with two LDS buffers. While step s is
+// computed, the activation and weight codes of step s+1 stream into the other
+// buffer by direct global-to-LDS loads (lane l of a wave instruction lands at
+// +16 l), and its scales are loaded into registers and decoded into LDS
+// after the compute. Rows are XOR-swizzled in 16-byte units so that the MFMA
+// operand reads are free of bank conflicts.
 //
 // Operands: A = activation codes (rows m), B = weight codes (columns n). A
 // lane holds 16 int8 of one row / column for one half of the block; the
@@ -18,148 +41,317 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128;        // activation rows per workgroup
 constexpr int BN = 128;        // weight rows per workgroup
-constexpr int KB = 8;          // 32-blocks per K step (one Q4_K super-block)
+constexpr int KB = 4;          // 32-blocks per K step
 constexpr int kThreads = 256;  // 4 waves, 2 x 2, each 64 x 64
+constexpr int kMagicBits = 0x4B400000;  // fp32 1.5 * 2^23
+constexpr float kMagic = 12582912.0f;
 
 template <int TYPE>
-struct Tile {
-  static constexpr int kQuantBytes = TYPE == kQ8_0 ? 32 * KB : 16 * KB;  // per row per step
+struct Cfg {
+  static constexpr int kWRow = TYPE == kQ8_0 ? 32 * KB : 16 * KB;  // weight bytes per row per step
+  static constexpr bool kHasMin = TYPE != kQ8_0;
 };
+
+// One LDS buffer: the codes of a K step (filled by direct loads) and its
+// decoded scales.
+template <int TYPE>
+struct Stage {
+  uint8_t a[BM * 32 * KB];       // activation codes, row r at 128 r, swizzled
+  uint8_t w[BN * Cfg<TYPE>::kWRow];  // weight codes, row r at kWRow r, swizzled
+  float sa[KB][BM];              // activation scale d
+  float asc[KB][BM];             // d * (code sum)
+  float sw[KB][BN];              // weight block scale
+  float wm[KB][BN];              // weight block min (Q4_K, Q4_0)
+};
+
+// 16-byte unit positions inside a row (XOR swizzle)
+__device__ __forceinline__ int a_pos(int r, int c) { return c ^ (r & 7); }  // 8 units per row
+template <int TYPE>
+__device__ __forceinline__ int w_pos(int r, int c) {
+  if constexpr (TYPE == kQ8_0) return c ^ (r & 7);  // 8 units per row
+  return c ^ ((r >> 2) & 3);                         // 4 units per row
+}
+
+// 16 bytes per lane from global memory straight into LDS; lane l of the wave
+// writes lds_base + 16 l (lds_base must be wave-uniform).
+__device__ __forceinline__ void lds_dma16(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+template <int TYPE>
+struct GemmCtx {
+  WeightView W;
+  ActView A;
+  int64_t n, nb, m, m0, n0;
+};
+
+// Direct global-to-LDS loads of step `st`'s codes into stage `S` (issued by
+// every wave; each wave instruction writes 1 KiB of the stage).
+template <int TYPE>
+__device__ __forceinline__ void issue_codes(const GemmCtx<TYPE>& g, Stage<TYPE>* __restrict__ S, int64_t st,
+                                            int wave, int lane) {
+  const int64_t blk0 = st * KB;
+  const int nblk = static_cast<int>(g.nb - blk0 < KB ? g.nb - blk0 : KB);
+  // activations: BM rows x 8 units = 16 instructions, 4 per wave
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int I = 4 * wave + i;
+    const int u = 64 * I + lane;  // unit index in the stage
+    const int r = u >> 3;
+    const int c = a_pos(r, u & 7);  // global unit stored at this position
+    const int64_t gm = g.m0 + r < g.m ? g.m0 + r : g.m - 1;
+    if (c < 2 * nblk) {
+      lds_dma16(g.A.codes(gm, blk0) + 16 * c, S->a + 1024 * I);
+    }
+  }
+  // weights
+  constexpr int kUnits = Cfg<TYPE>::kWRow / 16;       // units per row
+  constexpr int kInstr = BN * kUnits / 64 / 4;        // per wave
+  constexpr int kPerBlk = kUnits / KB;                // units per block (1 or 2)
+#pragma unroll
+  for (int i = 0; i < kInstr; ++i) {
+    const int I = kInstr * wave + i;
+    const int u = 64 * I + lane;
+    const int r = u / kUnits;
+    const int c = w_pos<TYPE>(r, u % kUnits);
+    const int64_t gn = g.n0 + r < g.n ? g.n0 + r : g.n - 1;
+    if (c < kPerBlk * nblk) {
+      const uint8_t* src =
+          g.W.row(gn) + g.W.hdr_bytes + (Cfg<TYPE>::kWRow / KB) * blk0 + 16 * c;
+      lds_dma16(src, S->w + 1024 * I);
+    }
+  }
+}
+
+// Scale data of step `st` into registers (decoded into LDS after the compute).
+struct ScaleRegs {
+  uint4 act;  // (d, sum) of two blocks of one activation row
+  uint4 wgt;  // Q4_K header / four fp32 block scales of one weight row
+};
+
+template <int TYPE>
+__device__ __forceinline__ ScaleRegs load_scales(const GemmCtx<TYPE>& g, int64_t st, int tid) {
+  ScaleRegs s;
+  const int64_t blk0 = st * KB;
+  const int nblk = static_cast<int>(g.nb - blk0 < KB ? g.nb - blk0 : KB);
+  const int r = tid >> 1;
+  const int h = tid & 1;  // blocks 2h, 2h+1
+  const int64_t gm = g.m0 + r < g.m ? g.m0 + r : g.m - 1;
+  // two 8-byte loads: a row's (d, sum) pairs are only 8-byte aligned, and the
+  // second block may lie past the last block of the row
+  const uint8_t* src = g.A.ds + 8 * (gm * g.nb + blk0 + 2 * h);
+  uint2 p0 = make_uint2(0, 0), p1 = make_uint2(0, 0);
+  if (2 * h < nblk) p0 = *reinterpret_cast<const uint2*>(src);
+  if (2 * h + 1 < nblk) p1 = *reinterpret_cast<const uint2*>(src + 8);
+  s.act = make_uint4(p0.x, p0.y, p1.x, p1.y);
+  s.wgt = make_uint4(0, 0, 0, 0);
+  if (tid < BN) {
+    const int64_t gn = g.n0 + tid < g.n ? g.n0 + tid : g.n - 1;
+    if constexpr (TYPE == kQ4_K) {
+      s.wgt = load16(g.W.row(gn) + 16 * (blk0 >> 3));
+    } else {
+      // 16 bytes of scales; the padded header region keeps this in bounds
+      s.wgt = load16(g.W.row(gn) + 4 * blk0);
+    }
+  }
+  return s;
+}
+
+template <int TYPE>
+__device__ __forceinline__ void store_scales(Stage<TYPE>* __restrict__ S, const ScaleRegs& s, int64_t st,
+                                             int tid) {
+  const int r = tid >> 1;
+  const int h = tid & 1;
+  const float d0 = __uint_as_float(s.act.x), d1 = __uint_as_float(s.act.z);
+  S->sa[2 * h][r] = d0;
+  S->asc[2 * h][r] = d0 * static_cast<float>(static_cast<int>(s.act.y));
+  S->sa[2 * h + 1][r] = d1;
+  S->asc[2 * h + 1][r] = d1 * static_cast<float>(static_cast<int>(s.act.w));
+  if (tid < BN) {
+    if constexpr (TYPE == kQ4_K) {
+      const float d = half_bits_to_float(s.wgt.x);
+      const float dmin = half_bits_to_float(s.wgt.x >> 16);
+      const int j0 = static_cast<int>((st * KB) & 7);
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) {
+        S->sw[jj][tid] = d * static_cast<float>(q4k_sc(s.wgt, j0 + jj));
+        S->wm[jj][tid] = dmin * static_cast<float>(q4k_mn(s.wgt, j0 + jj));
+      }
+    } else {
+      const float dw[4] = {__uint_as_float(s.wgt.x), __uint_as_float(s.wgt.y),
+                           __uint_as_float(s.wgt.z), __uint_as_float(s.wgt.w)};
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) {
+        S->sw[jj][tid] = dw[jj];
+        S->wm[jj][tid] = -8.0f * dw[jj];  // Q4_0: codes are nibble - 8
+      }
+    }
+  }
+}
+
+struct Acc {
+  v16f main[2][2];  // scale steps (VALU) and min terms (matrix core) accumulate here
+};
+
+// The MFMAs and scale steps of one K step from stage S.
+template <int TYPE>
+__device__ __forceinline__ void compute(const Stage<TYPE>* __restrict__ S, int nblk, int wm0, int wn0, int half,
+                                        int l32, const v16i& cinit, Acc& acc) {
+  for (int j = 0; j < nblk; ++j) {
+    v4i bop[2];
+    float sw[2], ncs[2];
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+      const int r = wn0 + 32 * tn + l32;
+      if constexpr (TYPE == kQ8_0) {
+        const uint4 w = *reinterpret_cast<const uint4*>(
+            S->w + Cfg<TYPE>::kWRow * r + 16 * w_pos<TYPE>(r, 2 * j + half));
+        bop[tn] = v4i{static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                      static_cast<int>(w.w)};
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(
+            S->w + Cfg<TYPE>::kWRow * r + 16 * w_pos<TYPE>(r, j) + 8 * half);
+        const uint32_t msk = 0x0F0F0F0Fu;
+        bop[tn] = v4i{static_cast<int>(w.x & msk), static_cast<int>((w.x >> 4) & msk),
+                      static_cast<int>(w.y & msk), static_cast<int>((w.y >> 4) & msk)};
+      }
+      sw[tn] = S->sw[j][r];
+      ncs[tn] = -kMagic * sw[tn];
+    }
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const int ra = wm0 + 32 * tm + l32;
+      const uint4 a = *reinterpret_cast<const uint4*>(S->a + 128 * ra + 16 * a_pos(ra, 2 * j + half));
+      const v4i aop = v4i{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z),
+                          static_cast<int>(a.w)};
+      // activation scales of this lane's 16 rows: 4 consecutive rows per quarter
+      float sa[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 s4 =
+            *reinterpret_cast<const float4*>(&S->sa[j][wm0 + 32 * tm + 8 * q + 4 * half]);
+        sa[4 * q + 0] = s4.x;
+        sa[4 * q + 1] = s4.y;
+        sa[4 * q + 2] = s4.z;
+        sa[4 * q + 3] = s4.w;
+      }
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) {
+        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop[tn], cinit, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float t;
+          if constexpr (TYPE == kQ4_K) {
+            t = fmaf(__int_as_float(c[v]), sw[tn], ncs[tn]);  // = round(S * sw)
+          } else {
+            t = static_cast<float>(c[v]) * sw[tn];
+          }
+          acc.main[tm][tn][v] = fmaf(t, sa[v], acc.main[tm][tn][v]);
+        }
+      }
+    }
+  }
+  // min terms on the matrix cores: K = 2 blocks per instruction
+  if constexpr (Cfg<TYPE>::kHasMin) {
+#pragma unroll
+    for (int i = 0; i < KB / 2; ++i) {
+      if (2 * i < nblk) {  // uniform
+        const int b = 2 * i + half;
+        const bool okb = b < nblk;
+        float af[2], bf[2];
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm) af[tm] = okb ? S->asc[b][wm0 + 32 * tm + l32] : 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn) bf[tn] = okb ? S->wm[b][wn0 + 32 * tn + l32] : 0.0f;
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < 2; ++tn)
+            acc.main[tm][tn] =
+                __builtin_amdgcn_mfma_f32_32x32x2f32(af[tm], bf[tn], acc.main[tm][tn], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// One K step: the codes (and scales) of step st+1 stream into `nxt` while
+// step st is computed from `cur`. `cur` and `nxt` are distinct LDS buffers;
+// declaring them restrict lets the compiler see that the compute's LDS reads
+// never wait for the direct loads into `nxt`.
+template <int TYPE>
+__device__ __forceinline__ bool step(const GemmCtx<TYPE>& g, const Stage<TYPE>* __restrict__ cur,
+                                     Stage<TYPE>* __restrict__ nxt, int64_t st, int64_t steps,
+                                     int tid, int wave, int lane, int wm0, int wn0, int half,
+                                     int l32, const v16i& cinit, Acc& acc) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into `cur` are done
+  __syncthreads();                // everyone's; the previous readers of `nxt` are done
+  const bool more = st + 1 < steps;
+  ScaleRegs sc;
+  if (more) {
+    // scale loads first: vmcnt retires in order, so waiting for them later
+    // does not wait for the code loads issued after them
+    sc = load_scales<TYPE>(g, st + 1, tid);
+    issue_codes<TYPE>(g, nxt, st + 1, wave, lane);
+  }
+  const int nblk = static_cast<int>(g.nb - st * KB < KB ? g.nb - st * KB : KB);
+  compute<TYPE>(cur, nblk, wm0, wn0, half, l32, cinit, acc);
+  if (more) {
+    asm volatile("" ::: "memory");  // keep the scale stores after the compute
+    store_scales<TYPE>(nxt, sc, st + 1, tid);
+  }
+  return more;
+}
 
 template <int TYPE>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n, int64_t nb,
                                                         ActView A, int64_t m,
                                                         float* __restrict__ y, int64_t ldy) {
-  constexpr int QB = Tile<TYPE>::kQuantBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[BM][32 * KB + 16];  // activation codes (+16: bank skew)
-  __shared__ __attribute__((aligned(16))) float2 s_ads[BM][KB];       // (d, sum)
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[BN][QB + 16];   // weight codes (+16: bank skew)
-  __shared__ __attribute__((aligned(16))) uint32_t s_wh[BN][KB];      // weight scales / header
+  __shared__ __attribute__((aligned(16))) Stage<TYPE> s0;
+  __shared__ __attribute__((aligned(16))) Stage<TYPE> s1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 1) * 64;  // wave's row offset in the tile
   const int wn0 = (wave & 1) * 64;   // wave's column offset in the tile
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
-  const int half = lane >> 5;  // which 16 elements of a block this lane holds
+  const int half = lane >> 5;        // which 16 elements of a block this lane holds
   const int l32 = lane & 31;
 
-  float acc[2][2][16];
+  GemmCtx<TYPE> g;
+  g.W = W;
+  g.A = A;
+  g.n = n;
+  g.nb = nb;
+  g.m = m;
+  g.m0 = static_cast<int64_t>(blockIdx.y) * BM;
+  g.n0 = static_cast<int64_t>(blockIdx.x) * BN;
+
+  Acc acc;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+      for (int v = 0; v < 16; ++v) acc.main[a][b][v] = 0.0f;
+  v16i cinit;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cinit[v] = TYPE == kQ4_K ? kMagicBits : 0;
 
   const int64_t steps = (nb + KB - 1) / KB;
-  for (int64_t st = 0; st < steps; ++st) {
-    const int64_t blk0 = st * KB;
-    const int nblk = static_cast<int>(nb - blk0 < KB ? nb - blk0 : KB);
+  // prologue: step 0 into s0
+  store_scales<TYPE>(&s0, load_scales<TYPE>(g, 0, tid), 0, tid);
+  issue_codes<TYPE>(g, &s0, 0, wave, lane);
 
-    // ---- global -> LDS
-    // activation codes: BM rows x (32*nblk) bytes, 16 B per thread-load
-    for (int i = tid; i < BM * 2 * KB; i += kThreads) {
-      const int r = i / (2 * KB);
-      const int c = i % (2 * KB);  // 16-byte chunk within the step
-      if (c < 2 * nblk) {
-        const int64_t gm = m0 + r < m ? m0 + r : m - 1;
-        *reinterpret_cast<uint4*>(&s_a[r][16 * c]) = load16(A.codes(gm, blk0) + 16 * c);
-      }
-    }
-    for (int i = tid; i < BM * KB; i += kThreads) {
-      const int r = i / KB;
-      const int c = i % KB;
-      if (c < nblk) {
-        const int64_t gm = m0 + r < m ? m0 + r : m - 1;
-        s_ads[r][c] = A.dsum(gm, blk0 + c);
-      }
-    }
-    // weight codes
-    for (int i = tid; i < BN * (QB / 16); i += kThreads) {
-      const int r = i / (QB / 16);
-      const int c = i % (QB / 16);
-      const int per_blk = QB / 16 / KB;  // 16-byte chunks per block (1 or 2)
-      if (c < per_blk * nblk) {
-        const int64_t gn = n0 + r < n ? n0 + r : n - 1;
-        const uint8_t* src = W.row(gn) + W.hdr_bytes + (QB / KB) * blk0 + 16 * c;
-        *reinterpret_cast<uint4*>(&s_w[r][16 * c]) = load_stream16(src);
-      }
-    }
-    // weight scales: Q4_K one 16-byte header per step, else one fp32 per block
-    for (int i = tid; i < BN * KB; i += kThreads) {
-      const int r = i / KB;
-      const int c = i % KB;
-      const int64_t gn = n0 + r < n ? n0 + r : n - 1;
-      if constexpr (TYPE == kQ4_K) {
-        if (c < 4) s_wh[r][c] = reinterpret_cast<const uint32_t*>(W.row(gn) + 16 * st)[c];
-      } else {
-        if (c < nblk) s_wh[r][c] = reinterpret_cast<const uint32_t*>(W.row(gn))[blk0 + c];
-      }
-    }
-    __syncthreads();
-
-    // ---- per block: MFMA on the 2 x 2 tiles, then the fp32 scale epilogue
-    for (int j = 0; j < nblk; ++j) {
-      v4i bop[2];
-      float sw[2], wm[2];
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
-        const int r = wn0 + 32 * tn + l32;
-        if constexpr (TYPE == kQ8_0) {
-          const uint4 w = *reinterpret_cast<const uint4*>(&s_w[r][32 * j + 16 * half]);
-          bop[tn] = v4i{static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
-                        static_cast<int>(w.w)};
-        } else {
-          const uint2 w = *reinterpret_cast<const uint2*>(&s_w[r][16 * j + 8 * half]);
-          const uint32_t msk = 0x0F0F0F0Fu;
-          bop[tn] = v4i{static_cast<int>(w.x & msk), static_cast<int>((w.x >> 4) & msk),
-                        static_cast<int>(w.y & msk), static_cast<int>((w.y >> 4) & msk)};
-        }
-        if constexpr (TYPE == kQ4_K) {
-          const uint4 h = make_uint4(s_wh[r][0], s_wh[r][1], s_wh[r][2], s_wh[r][3]);
-          sw[tn] = half_bits_to_float(h.x) * static_cast<float>(q4k_sc(h, j));
-          wm[tn] = half_bits_to_float(h.x >> 16) * static_cast<float>(q4k_mn(h, j));
-        } else {
-          sw[tn] = __uint_as_float(s_wh[r][j]);
-          wm[tn] = 0.0f;
-        }
-      }
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm) {
-        const int ra = wm0 + 32 * tm + l32;
-        const uint4 a = *reinterpret_cast<const uint4*>(&s_a[ra][32 * j + 16 * half]);
-        const v4i aop = v4i{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z),
-                            static_cast<int>(a.w)};
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          v16i c = {0};
-          c = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop[tn], c, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rm = wm0 + 32 * tm + 8 * (v >> 2) + 4 * half + (v & 3);
-            const float2 ds = s_ads[rm][j];
-            const int asum = __float_as_int(ds.y);
-            if constexpr (TYPE == kQ4_K) {
-              acc[tm][tn][v] = fmaf(ds.x, fmaf(sw[tn], static_cast<float>(c[v]),
-                                               wm[tn] * static_cast<float>(asum)),
-                                    acc[tm][tn][v]);
-            } else if constexpr (TYPE == kQ4_0) {
-              acc[tm][tn][v] = fmaf(ds.x * sw[tn], static_cast<float>(c[v] - 8 * asum),
-                                    acc[tm][tn][v]);
-            } else {
-              acc[tm][tn][v] = fmaf(ds.x * sw[tn], static_cast<float>(c[v]), acc[tm][tn][v]);
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
+  for (int64_t st = 0; st < steps; st += 2) {
+    if (!step<TYPE>(g, &s0, &s1, st, steps, tid, wave, lane, wm0, wn0, half, l32, cinit, acc))
+      break;
+    if (!step<TYPE>(g, &s1, &s0, st + 1, steps, tid, wave, lane, wm0, wn0, half, l32, cinit,
+                    acc))
+      break;
   }
 
   // ---- store: lane holds column n = l32 and 16 rows of each 32 x 32 tile
@@ -167,12 +359,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n,
   for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
-      const int64_t gn = n0 + wn0 + 32 * tn + l32;
+      const int64_t gn = g.n0 + wn0 + 32 * tn + l32;
       if (gn >= n) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t gm = m0 + wm0 + 32 * tm + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (gm < m) y[gm * ldy + gn] = acc[tm][tn][v];
+        const int64_t gm = g.m0 + wm0 + 32 * tm + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (gm < m) y[gm * ldy + gn] = acc.main[tm][tn][v];
       }
     }
 }
