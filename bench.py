@@ -199,6 +199,7 @@ class DecodeModel:
             act = 4 * k * self.batch if fused else qblk.qblk_act_bytes(self.batch, k)
             alg = (qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + act + 4 * n * self.batch) * len(layers)
             per[g] = {"n": n, "k": k, "us": round(1e6 * sec / len(layers), 3),
+                      "alg_bytes": alg // len(layers),
                       "GBps": round(alg / sec / 1e9, 1), "fused_quantization": fused}
             tot_b += alg
             tot_s += sec
@@ -232,8 +233,15 @@ def main():
     log(f"batch 1: {ms_tok:.3f} ms/token, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% "
         f"of HBM peak)")
     tot_b, tot_s, per_group = m1.kernel_times(m1.layers)
-    achieved = tot_b / tot_s / 1e9
-    log(f"gemv kernel (graphs of back-to-back launches): {achieved:.1f} GB/s; {per_group}")
+    all_gemv = tot_b / tot_s / 1e9
+    # the dominant kernel: gemv_kernel<Q4_K, batch 1, 4 rows per wave, 1 chunk>
+    # streams gate_up and down (82% of the weight bytes)
+    dom = [per_group[g] for g in DOMINANT_GROUPS]
+    dom_bytes = sum(p["alg_bytes"] for p in dom)
+    dom_sec = sum(p["us"] for p in dom) * 1e-6
+    achieved = dom_bytes / dom_sec / 1e9
+    log(f"gemv kernels (graphs of back-to-back launches): all {all_gemv:.1f} GB/s, "
+        f"{DOMINANT_KERNEL} {achieved:.1f} GB/s; {per_group}")
     del g1
 
     m4 = m1
@@ -288,12 +296,15 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel<Q4_K, batch 1>",
+            "kernel": DOMINANT_KERNEL,
+            "launches": "gate_up 57344x8192 and down 8192x28672 of every layer",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profile(),
+            "traffic": traffic_from_profile(GEMV_TRAFFIC, GEMV_SOURCES),
+            "alg_bytes_per_launch": dom_bytes // len(dom),
+            "all_gemv_GBps": round(all_gemv, 1),
             "per_launch": per_group,
         },
         "secondary": secondary,
@@ -305,25 +316,31 @@ def main():
 # ---------------------------------------------------------------- HBM traffic
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_q4k_70b_decode_traffic.md")
-KERNEL_SOURCES = ["block_quantized_qblk_amd/csrc/gemv.hip",
-                  "block_quantized_qblk_amd/csrc/qblk_device.h"]
+DOMINANT_KERNEL = "gemv_kernel<3, 1, 4, 1>"      # <Q4_K, batch, rows per wave, chunks>
+DOMINANT_GROUPS = ("gate_up", "down")
+GEMV_TRAFFIC = os.path.join(ROOT, "profiles", "gemv_q4k_70b_decode_traffic.md")
+GEMV_SOURCES = ["block_quantized_qblk_amd/csrc/gemv.hip",
+                "block_quantized_qblk_amd/csrc/qblk_device.h"]
+GEMM_TRAFFIC = os.path.join(ROOT, "profiles", "gemm_q4k_512x14336x4096.md")
+GEMM_SOURCES = ["block_quantized_qblk_amd/csrc/gemm.hip",
+                "block_quantized_qblk_amd/csrc/qblk_device.h"]
 
 
-def kernel_sha256():
+def sources_sha256(sources):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def traffic_from_profile():
-    """Measured HBM bytes per GEMV launch from the committed counter summary,
-    or None when it is missing or was taken on different kernel sources."""
+def traffic_from_profile(path, sources):
+    """Measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a
+    device copy) from a committed counter summary, or None when the summary is
+    missing or was taken on different kernel sources."""
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(path).read()
     except OSError:
         return None
     import re
@@ -331,14 +348,16 @@ def traffic_from_profile():
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_sha256") != kernel_sha256():
+    if rec.get("sources_sha256") != sources_sha256(sources):
         return None
     return rec["hbm_bytes_per_launch"]
 
 
 def traffic_probe(torch, qblk, synth, dev):
-    """Calibration copy of 1 GiB, then the four GEMVs of four 70B-shaped
-    layers once (batch 1). Prints the algorithmic bytes of each GEMV launch."""
+    """For rocprofv3 --pmc runs: a 1 GiB device copy (calibration), one decode
+    token of four 70B-shaped layers at batch 1 (per layer: qkv, o, gate_up,
+    down), then one Q4_K GEMM of 512 x 14336 x 4096. Prints the algorithmic
+    bytes of every GEMV and GEMM launch, in launch order."""
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -348,12 +367,25 @@ def traffic_probe(torch, qblk, synth, dev):
     m = DecodeModel(torch, qblk, synth, synth.LAYER_70B, 4, 5000, "student_t", 1, dev)
     m.token()
     torch.cuda.synchronize()
-    alg = [{"group": g, "n": n, "k": k,
-            "alg_bytes": qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + 4 * n
-            + (4 * k if m.fused(k, n) else qblk.qblk_act_bytes(1, k))}
-           for _ in range(4) for g, _, n, k in m.groups]
-    print(json.dumps({"copy_bytes_each_way": 1 << 30, "gemv_launches": alg,
-                      "kernel_sha256": kernel_sha256()}))
+    gemv = [{"group": g, "n": n, "k": k,
+             "alg_bytes": qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + 4 * n
+             + (4 * k if m.fused(k, n) else qblk.qblk_act_bytes(1, k))}
+            for _ in range(4) for g, _, n, k in m.groups]
+    del m
+    n, k, mm = 14336, 4096, 512
+    w = synth.torch_weights("outliers", 4000, n, k, device=dev)
+    wq = qblk.qblk_pack_weights(qblk.Q4_K, w)
+    xq = qblk.qblk_quantize_act(synth.torch_activations(4099, mm, k, device=dev))
+    y = torch.empty((mm, n), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    qblk.qblk_gemm(qblk.Q4_K, wq, n, k, xq, mm, y=y)
+    torch.cuda.synchronize()
+    gemm = {"m": mm, "n": n, "k": k, "alg_bytes": qblk.qblk_weight_bytes(qblk.Q4_K, n, k)
+            + qblk.qblk_act_bytes(mm, k) + 4 * mm * n}
+    print(json.dumps({"copy_bytes_each_way": 1 << 30, "gemv_launches": gemv,
+                      "gemm_launch": gemm,
+                      "gemv_sources_sha256": sources_sha256(GEMV_SOURCES),
+                      "gemm_sources_sha256": sources_sha256(GEMM_SOURCES)}))
 
 
 def m_bytes(qblk, synth, layers):
@@ -394,14 +426,17 @@ def timed_launches(torch, fn, iters):
     return 1e3 * sum(a.elapsed_time(b) for a, b in ev) / iters   # us
 
 
-def gemm_bench(torch, qblk, synth, dev, iters):
+def gemm_bench(torch, qblk, synth, dev, iters, copies=16):
     """Q4_K prefill GEMM 512 x 14336 x 4096, and M in {1, 8, 64} against the
-    GEMV on the same weights."""
+    GEMV on the same weights; launches rotate over `copies` packed weight
+    copies (16 x 33 MB, twice the 256 MB last-level cache)."""
     Q4_K = qblk.Q4_K
     n, k = 14336, 4096
-    w = synth.torch_weights("outliers", 4000, n, k, device=dev)
-    wq = qblk.qblk_pack_weights(Q4_K, w)
-    del w
+    wqs = []
+    for c in range(copies):
+        w = synth.torch_weights("outliers", 4000 + c, n, k, device=dev)
+        wqs.append(qblk.qblk_pack_weights(Q4_K, w))
+        del w
     res = {}
     for m in (512, 1, 8, 64):
         x = synth.torch_activations(4099, m, k, device=dev)
@@ -412,19 +447,25 @@ def gemm_bench(torch, qblk, synth, dev, iters):
         if m <= 64:
             fns.append(("gemv", qblk.qblk_gemv))
         for fname, f in fns:
-            us = timed_launches(torch, lambda i: f(Q4_K, wq, n, k, xq, m, y=y), iters)
+            us = timed_launches(torch, lambda i: f(Q4_K, wqs[i % copies], n, k, xq, m, y=y),
+                                iters)
             ops = 2.0 * m * n * k
-            row[fname] = {"us": round(us, 3), "TOPS": round(ops / (us * 1e-6) / 1e12, 2)}
+            row[fname] = {"us": round(us, 3), "TOPS": round(ops / (us * 1e-6) / 1e12, 2),
+                          "weight_GBps": round(qblk.qblk_weight_bytes(Q4_K, n, k)
+                                               / (us * 1e-6) / 1e9, 1)}
         res[f"m{m}"] = row
         log(f"gemm m={m}: {row}")
+    del wqs
+    torch.cuda.empty_cache()
     g = res["m512"]["gemm"]
     return {
         "workload": "q4_k_gemm_512x14336x4096",
         "TOPS": g["TOPS"],
         "us": g["us"],
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<Q4_K>", "achieved": g["TOPS"],
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<3>", "achieved": g["TOPS"],
                      "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(g["TOPS"] / INT8_PEAK_TOPS, 4), "traffic": None},
+                     "frac": round(g["TOPS"] / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic_from_profile(GEMM_TRAFFIC, GEMM_SOURCES)},
         "crossover": res,
     }
 
