@@ -6,8 +6,10 @@ each q/k/v (8192/1024/1024 x 8192), o (8192 x 8192), gate/up (28672 x 8192)
 and down (8192 x 28672) - one full 38.5 GB weight stream per token. q/k/v
 share an input and are packed as one 10240-row matrix, gate/up as one
 57344-row matrix (rows are independent in the packed layout, so this changes
-only the launch count). Per layer: four activation quantizations and four
-GEMVs, captured in a HIP graph per token.
+only the launch count). Per layer: four products, each one launch of
+qblk_gemv_f32 (activation quantization fused into the GEMV), captured in a
+HIP graph per token. The same token with a separate quantization launch
+before each GEMV is reported beside it.
 
 Headline value: effective packed-weight GB/s = weight bytes per token / time
 per token (batch 1). Also reported: batch 4, the GEMV kernel's roofline
@@ -120,39 +122,43 @@ class DecodeModel:
                 packed[gname] = buf
             self.layers.append(packed)
         torch.cuda.synchronize()
-        self.x = {g: synth.torch_activations(seed0 + 900 + i, batch, k, device=dev)
-                  for i, (g, _, _, k) in enumerate(self.groups)}
-        self.xq = {g: torch.empty(qblk.qblk_act_bytes(batch, k), dtype=torch.uint8, device=dev)
-                   for g, _, _, k in self.groups}
-        self.y = {g: torch.empty((batch, n), dtype=torch.float32, device=dev)
-                  for g, _, n, _ in self.groups}
+        self.synth = synth
+        self.two_step = False
+        self.set_batch(batch, seed0 + 900)
         self.weight_bytes = sum(qblk.qblk_weight_bytes(Q4_K, n, k)
                                 for _, _, n, k in self.groups) * layers
 
-    # the fused entry point repeats the quantization in every workgroup: it
-    # beats quantize + GEMV (one kernel boundary more) only on small matrices
-    FUSED_MAX_ELEMS = 32 << 20
+    def set_batch(self, batch, seed):
+        torch, qblk = self.torch, self.qblk
+        dev = self.layers[0]["qkv"].device
+        self.batch = batch
+        self.x = {g: self.synth.torch_activations(seed + i, batch, k, device=dev)
+                  for i, (g, _, _, k) in enumerate(self.groups)}
+        self.xq = {g: torch.empty(qblk.qblk_act_bytes(batch, k), dtype=torch.uint8, device=dev)
+                   for g, _, _, k in self.groups}
+        self.work = {g: torch.zeros(qblk.qblk_gemv_f32_work_bytes(batch, k), dtype=torch.uint8,
+                                    device=dev)
+                     for g, _, _, k in self.groups}
+        self.y = {g: torch.empty((batch, n), dtype=torch.float32, device=dev)
+                  for g, _, n, _ in self.groups}
 
-    def fused(self, k, n=None):
-        n = n if n is not None else max(gn for _, _, gn, gk in self.groups if gk == k)
-        return (n * k <= self.FUSED_MAX_ELEMS
-                and self.batch <= self.qblk.qblk_gemv_f32_max_batch(k))
+    def gemv(self, g, n, k, packed):
+        """One group's product for the current activation: quantization fused
+        into the GEMV (qblk_gemv_f32: one launch), or, with two_step,
+        qblk_quantize_act then qblk_gemv (two launches)."""
+        qblk = self.qblk
+        if self.two_step:
+            qblk.qblk_quantize_act(self.x[g], out=self.xq[g])
+            qblk.qblk_gemv(qblk.Q4_K, packed[g], n, k, self.xq[g], self.batch, y=self.y[g])
+        else:
+            qblk.qblk_gemv_f32(qblk.Q4_K, packed[g], n, k, self.x[g], y=self.y[g],
+                               work=self.work[g])
 
     def token(self, layers=None):
-        """One decode token: per layer and group, the activation quantization
-        fused into the GEMV when its codes fit local memory, else
-        qblk_quantize_act followed by qblk_gemv."""
-        qblk = self.qblk
-        for li, packed in enumerate(self.layers if layers is None else layers):
+        """One decode token: per layer, the four group products."""
+        for packed in self.layers if layers is None else layers:
             for g, _, n, k in self.groups:
-                fused = self.fused(k, n)
-                if not fused:
-                    qblk.qblk_quantize_act(self.x[g], out=self.xq[g])
-                if fused:
-                    qblk.qblk_gemv_f32(qblk.Q4_K, packed[g], n, k, self.x[g], y=self.y[g])
-                else:
-                    qblk.qblk_gemv(qblk.Q4_K, packed[g], n, k, self.xq[g], self.batch,
-                                   y=self.y[g])
+                self.gemv(g, n, k, packed)
 
     def capture(self, layers=None):
         torch = self.torch
@@ -170,25 +176,25 @@ class DecodeModel:
         return graph
 
     def kernel_times(self, layers):
-        """Per-launch GEMV time: for each group, one HIP graph of its GEMV over
-        `layers` layers back to back (the activation quantized once before),
-        bracketed by HIP events on the launch stream; time / launches is the
-        kernel's boundary-to-boundary duration, as a kernel trace reports it.
-        Returns (algorithmic bytes, seconds, per-group table)."""
+        """Per-launch GEMV time: for each group, one HIP graph of its product
+        over `layers` layers back to back, bracketed by HIP events on the
+        launch stream; time / launches is the kernel's boundary-to-boundary
+        duration, as a kernel trace reports it (two-step: the GEMV alone, the
+        activation quantized once before). Returns (algorithmic bytes,
+        seconds, per-group table)."""
         torch, qblk = self.torch, self.qblk
         per, tot_b, tot_s = {}, 0, 0.0
         for g, _, n, k in self.groups:
-            fused = self.fused(k, n)
-            if not fused:
+            if self.two_step:
                 qblk.qblk_quantize_act(self.x[g], out=self.xq[g])
 
             def launches():
                 for packed in layers:
-                    if fused:
-                        qblk.qblk_gemv_f32(qblk.Q4_K, packed[g], n, k, self.x[g], y=self.y[g])
-                    else:
+                    if self.two_step:
                         qblk.qblk_gemv(qblk.Q4_K, packed[g], n, k, self.xq[g], self.batch,
                                        y=self.y[g])
+                    else:
+                        self.gemv(g, n, k, packed)
             launches()
             torch.cuda.synchronize()
             graph = torch.cuda.CUDAGraph()
@@ -196,14 +202,21 @@ class DecodeModel:
                 launches()
             sec = time_replays(torch, [graph], 3, 1) * 1e-3
             del graph
-            act = 4 * k * self.batch if fused else qblk.qblk_act_bytes(self.batch, k)
-            alg = (qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + act + 4 * n * self.batch) * len(layers)
+            alg = alg_bytes(qblk, n, k, self.batch, not self.two_step) * len(layers)
             per[g] = {"n": n, "k": k, "us": round(1e6 * sec / len(layers), 3),
                       "alg_bytes": alg // len(layers),
-                      "GBps": round(alg / sec / 1e9, 1), "fused_quantization": fused}
+                      "GBps": round(alg / sec / 1e9, 1)}
             tot_b += alg
             tot_s += sec
         return tot_b, tot_s, per
+
+
+def alg_bytes(qblk, n, k, batch, fused):
+    """Algorithmic bytes of one product launch: packed weights, the
+    activation as the launch reads it (fp32 when the quantization is fused,
+    else the quantized buffer) and the fp32 output."""
+    act = 4 * k * batch if fused else qblk.qblk_act_bytes(batch, k)
+    return qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + act + 4 * n * batch
 
 
 def main():
@@ -232,29 +245,31 @@ def main():
     value = m1.weight_bytes / (ms_tok * 1e-3) / 1e9
     log(f"batch 1: {ms_tok:.3f} ms/token, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% "
         f"of HBM peak)")
+    del g1
     tot_b, tot_s, per_group = m1.kernel_times(m1.layers)
     all_gemv = tot_b / tot_s / 1e9
-    # the dominant kernel: gemv_kernel<Q4_K, batch 1, 4 rows per wave, 1 chunk>
-    # streams gate_up and down (82% of the weight bytes)
+    # the dominant kernel streams gate_up and down (82% of the weight bytes)
     dom = [per_group[g] for g in DOMINANT_GROUPS]
     dom_bytes = sum(p["alg_bytes"] for p in dom)
     dom_sec = sum(p["us"] for p in dom) * 1e-6
     achieved = dom_bytes / dom_sec / 1e9
     log(f"gemv kernels (graphs of back-to-back launches): all {all_gemv:.1f} GB/s, "
         f"{DOMINANT_KERNEL} {achieved:.1f} GB/s; {per_group}")
-    del g1
 
-    m4 = m1
-    m4.batch = 4
-    m4.x = {g: synth.torch_activations(5950 + i, 4, k, device=dev)
-            for i, (g, _, _, k) in enumerate(m4.groups)}
-    m4.xq = {g: torch.empty(qblk.qblk_act_bytes(4, k), dtype=torch.uint8, device=dev)
-             for g, _, _, k in m4.groups}
-    m4.y = {g: torch.empty((4, n), dtype=torch.float32, device=dev) for g, _, n, _ in m4.groups}
-    g4 = m4.capture()
+    # the same token with the activation quantized by its own launch
+    m1.two_step = True
+    g2 = m1.capture()
+    ms_two = time_replays(torch, [g2], max(5, args.steps // 3), 1)
+    del g2
+    _, _, per_two = m1.kernel_times(m1.layers)
+    log(f"batch 1, quantize + GEMV launches: {ms_two:.3f} ms/token; GEMV alone {per_two}")
+    m1.two_step = False
+
+    m1.set_batch(4, 5950)
+    g4 = m1.capture()
     ms_tok4 = time_replays(torch, [g4], max(5, args.steps // 3), 1)
-    log(f"batch 4: {ms_tok4:.3f} ms/step, {m4.weight_bytes / (ms_tok4 * 1e-3) / 1e9:.1f} GB/s")
-    del g4, m1, m4
+    log(f"batch 4: {ms_tok4:.3f} ms/step, {m1.weight_bytes / (ms_tok4 * 1e-3) / 1e9:.1f} GB/s")
+    del g4, m1
     torch.cuda.empty_cache()
 
     secondary = {}
@@ -289,10 +304,11 @@ def main():
             "tokens_per_s": round(1e3 / ms_tok, 2),
             "batch4_ms_per_step": round(ms_tok4, 6),
             "batch4_GBps": round(m_bytes(qblk, synth, args.layers) / (ms_tok4 * 1e-3) / 1e9, 2),
-            "launches_per_token": 8 * args.layers,
-            "activation_quantization": "qblk_quantize_act before each GEMV (the fused "
-                                       "qblk_gemv_f32 is used only for matrices of at most "
-                                       "32M weights, where it is faster)",
+            "launches_per_token": 4 * args.layers,
+            "activation_quantization": "fused into each GEMV launch (qblk_gemv_f32)",
+            "two_step_ms_per_step": round(ms_two, 6),
+            "two_step_GBps": round(m_bytes(qblk, synth, args.layers) / (ms_two * 1e-3) / 1e9, 2),
+            "two_step_gemv_per_launch": per_two,
         },
         "roofline": {
             "bound": "hbm",
@@ -316,7 +332,7 @@ def main():
 # ---------------------------------------------------------------- HBM traffic
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DOMINANT_KERNEL = "gemv_kernel<3, 1, 4, 1>"      # <Q4_K, batch, rows per wave, chunks>
+DOMINANT_KERNEL = "gemv_kernel<3, 1, 4, 1, true>"   # <Q4_K, batch, rows/wave, chunks, in-launch quantization>
 DOMINANT_GROUPS = ("gate_up", "down")
 GEMV_TRAFFIC = os.path.join(ROOT, "profiles", "gemv_q4k_70b_decode_traffic.md")
 GEMV_SOURCES = ["block_quantized_qblk_amd/csrc/gemv.hip",
@@ -367,9 +383,7 @@ def traffic_probe(torch, qblk, synth, dev):
     m = DecodeModel(torch, qblk, synth, synth.LAYER_70B, 4, 5000, "student_t", 1, dev)
     m.token()
     torch.cuda.synchronize()
-    gemv = [{"group": g, "n": n, "k": k,
-             "alg_bytes": qblk.qblk_weight_bytes(qblk.Q4_K, n, k) + 4 * n
-             + (4 * k if m.fused(k, n) else qblk.qblk_act_bytes(1, k))}
+    gemv = [{"group": g, "n": n, "k": k, "alg_bytes": alg_bytes(qblk, n, k, 1, True)}
             for _ in range(4) for g, _, n, k in m.groups]
     del m
     n, k, mm = 14336, 4096, 512

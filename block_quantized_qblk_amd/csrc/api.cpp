@@ -122,17 +122,24 @@ QBLK_EXPORT int qblk_gemv_f32_max_batch(int64_t k) {
   return static_cast<int>(qblk::gemv_f32_max_batch(k));
 }
 
+QBLK_EXPORT size_t qblk_gemv_f32_work_bytes(int64_t batch, int64_t k) {
+  if (batch < 0 || k <= 0 || k % 32 != 0 || k > kMaxK || batch > qblk::gemv_f32_max_batch(k))
+    return 0;
+  return static_cast<size_t>(qblk::gemv_f32_work_bytes(batch, k));
+}
+
 QBLK_EXPORT int qblk_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
-                              int64_t ldx, int64_t batch, float* y, int64_t ldy,
+                              int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
                               hipStream_t stream) {
   const int st = check_product(type, wq, n, k, x, batch, y, ldy);
   if (st != QBLK_OK || n == 0 || batch == 0) return st;
+  if (work == nullptr) return QBLK_ERR_ARG;
   if (ldx < k) return QBLK_ERR_SHAPE;
-  if (!aligned(x, 16) || ldx % 4 != 0) return QBLK_ERR_ALIGN;
+  if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(work, 256)) return QBLK_ERR_ALIGN;
   if (batch > qblk::gemv_f32_max_batch(k)) return QBLK_ERR_UNSUPPORTED;
   if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
-  return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, stream));
+  return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, work, stream));
 }
 
 QBLK_EXPORT int qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,

@@ -73,7 +73,100 @@ struct GemvArgs {
   int64_t ldx;
   float* y;
   int64_t ldy;
+  // in-kernel quantization handoff (SYNC variants): the first workgroups
+  // quantize 64-block slices of x into the workspace activation buffer
+  // (aq/ads alias it) and tag each slice in 8 flag copies
+  uint8_t* xq_codes;
+  uint8_t* xq_ds;
+  uint64_t* flags;     // [8][flag_stride] u64
+  uint32_t nslices;    // ceil(nb / 64)
+  uint32_t flag_stride;
 };
+
+// ---------------------------------------------------------------- in-kernel handoff
+// A launch-unique tag: the dispatch id of the packet (counts dispatches per
+// hardware queue) mixed with the packet's address (which identifies the
+// queue), so a flag left in the workspace by an earlier launch never matches.
+extern "C" __device__ uint64_t qblk_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+__device__ __forceinline__ uint64_t launch_tag() {
+  const uint64_t id = qblk_llvm_dispatch_id();
+  const uint64_t p = reinterpret_cast<uint64_t>(__builtin_amdgcn_dispatch_ptr());
+  return (id * 0x9E3779B97F4A7C15ull) ^ (p << 1) ^ 1ull;  // never 0 for a zeroed workspace
+}
+
+// Workgroup quantizes slice `sl` (blocks 64*sl .. 64*sl+63) of the B rows
+// of x into the workspace activation buffer with the qblk_quantize_act
+// arithmetic: one block per quad of threads, 8 elements per thread. The
+// stores are agent-scope atomic stores, which the L2 writes through to
+// memory, so they are visible to every XCD once complete.
+template <int B>
+__device__ __forceinline__ void quantize_slice(const GemvArgs& g, uint32_t sl) {
+  const uint32_t blk = (sl << 6) + (threadIdx.x >> 2);
+  const uint32_t sub = threadIdx.x & 3;
+  if (blk >= g.nb) return;  // whole quads
+  const uint32_t k = g.nb * 32u;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const float* src = g.x + b * g.ldx + 32u * blk + 8u * sub;
+    const float4 v0 = *reinterpret_cast<const float4*>(src);
+    const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+    const float e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const Q8Group q = quantize_group8(e);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(g.xq_codes + b * k + 32u * blk + 8u * sub),
+                       static_cast<uint64_t>(q.codes.x) | static_cast<uint64_t>(q.codes.y) << 32,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (sub == 0)
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(g.xq_ds + 8u * (b * g.nb + blk)),
+                         static_cast<uint64_t>(__float_as_uint(q.d)) |
+                             static_cast<uint64_t>(static_cast<uint32_t>(q.sum)) << 32,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Producer side: workgroups below nslices quantize slices wg, wg + grid, ...
+// and publish each. Every wave waits until its (write-through) stores have
+// completed, the workgroup meets at a barrier, then one wave stores the
+// slice's tag into each of the 8 flag copies. This is the hardware form of
+// release ordering for atomic stores; a release fence would in addition
+// write back the whole L2 of the XCD, which nothing here needs and which
+// took 3-5 us per launch on MI355X while the weight stream was running.
+template <int B>
+__device__ __forceinline__ void produce(const GemvArgs& g, uint64_t tag) {
+  for (uint32_t sl = blockIdx.x; sl < g.nslices; sl += gridDim.x) {
+    quantize_slice<B>(g, sl);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+    __syncthreads();
+    if (threadIdx.x < 8)
+      __hip_atomic_store(g.flags + threadIdx.x * g.flag_stride + sl, tag, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Consumer side: the workgroup polls the flag copy of its index mod 8 (one
+// relaxed load per slice, spread over its threads) until every slice carries
+// this launch's tag. Activation codes are read only after that, so no cache
+// holds a line of them from before this launch (the kernel start invalidated
+// the caches). The wait is bounded: after about 20 ms the workgroup
+// quantizes every slice itself (the same bytes the producers write), so the
+// kernel finishes with the right result even if the producers were never
+// scheduled. All exits are decided by workgroup-wide reductions.
+template <int B>
+__device__ __forceinline__ void wait_slices(const GemvArgs& g, uint64_t tag) {
+  const uint64_t* f = g.flags + (blockIdx.x & 7u) * g.flag_stride;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    int pending = 0;
+    for (uint32_t sl = threadIdx.x; sl < g.nslices; sl += 256u)
+      pending |= __hip_atomic_load(f + sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag;
+    if (!__syncthreads_or(pending)) return;
+    const int late = __builtin_amdgcn_s_memrealtime() - t0 > 2000000ull;  // 100 MHz clock
+    if (__syncthreads_or(late)) break;
+  }
+  for (uint32_t sl = 0; sl < g.nslices; ++sl) quantize_slice<B>(g, sl);
+  __threadfence();
+  __syncthreads();
+}
 
 // The per-block arithmetic of one weight row against B activation rows, in
 // one fixed order for every kernel variant (so that all variants, fused or
@@ -110,13 +203,22 @@ __device__ __forceinline__ void block_fma(uint32_t lane, const WChunk<TYPE>& w,
 
 // Classic variant: each wave issues the loads of U chunks for its R rows,
 // then computes them; occupancy hides the latency. Best for large matrices.
-template <int TYPE, int B, int R, int U>
+// SYNC: the activation is quantized inside the launch (produce /
+// wait_slices); the first chunks' weight loads are issued before the wait.
+template <int TYPE, int B, int R, int U, bool SYNC = false>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
   const uint32_t lane = threadIdx.x & 63;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t row0 = wave * R;
-  if (row0 >= g.n) return;  // whole wave
+  uint64_t tag = 0;
+  if constexpr (SYNC) {
+    tag = launch_tag();
+    produce<B>(g, tag);
+  } else {
+    if (row0 >= g.n) return;  // whole wave
+  }
+  const bool active = !SYNC || row0 < g.n;  // SYNC: every wave takes part in the waits
   const uint8_t* wrow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -132,7 +234,56 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 
-  for (uint32_t c0 = 0; c0 < nchunks; c0 += U) {
+  auto load_weights = [&](uint32_t c0, WChunk<TYPE>(&w)[R][U], WScale<TYPE>(&s)[R][U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t blk = ((c0 + u) << 6) + lane;
+      if (active && blk < g.nb) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) load_block<TYPE>(wrow[r], g.hdr_bytes, blk, w[r][u], s[r][u]);
+      }
+    }
+  };
+  auto load_acts = [&](uint32_t c0, int u, uint4(&a)[B][U][2], float2(&ds)[B][U]) {
+    const uint32_t blk = ((c0 + u) << 6) + lane;
+    if (blk < g.nb) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const uint8_t* ap = g.aq + b * k;
+        a[b][u][0] = load16(ap + 32u * blk);
+        a[b][u][1] = load16(ap + (32u * blk + 16u));
+        ds[b][u] = *reinterpret_cast<const float2*>(g.ads + 8u * (b * g.nb) + 8u * blk);
+      }
+    }
+  };
+  auto compute = [&](uint32_t c0, const WChunk<TYPE>(&w)[R][U], const WScale<TYPE>(&s)[R][U],
+                     const uint4(&a)[B][U][2], const float2(&ds)[B][U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t blk = ((c0 + u) << 6) + lane;
+      if (blk < g.nb) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) block_fma<TYPE, B>(lane, w[r][u], s[r][u], a, ds, u, acc[r]);
+      }
+    }
+  };
+
+  uint32_t c_start = 0;
+  if constexpr (SYNC) {
+    // first U chunks: weight loads in flight while the activation is awaited
+    WChunk<TYPE> w[R][U];
+    WScale<TYPE> s[R][U];
+    load_weights(0, w, s);
+    wait_slices<B>(g, tag);
+    if (!active) return;
+    uint4 a[B][U][2];
+    float2 ds[B][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_acts(0, u, a, ds);
+    compute(0, w, s, a, ds);
+    c_start = U;
+  }
+  for (uint32_t c0 = c_start; c0 < nchunks; c0 += U) {
     WChunk<TYPE> w[R][U];
     WScale<TYPE> s[R][U];
     uint4 a[B][U][2];
@@ -143,23 +294,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
       if (blk < g.nb) {
 #pragma unroll
         for (int r = 0; r < R; ++r) load_block<TYPE>(wrow[r], g.hdr_bytes, blk, w[r][u], s[r][u]);
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const uint8_t* ap = g.aq + b * k;
-          a[b][u][0] = load16(ap + 32u * blk);
-          a[b][u][1] = load16(ap + (32u * blk + 16u));
-          ds[b][u] = *reinterpret_cast<const float2*>(g.ads + 8u * (b * g.nb) + 8u * blk);
-        }
       }
+      load_acts(c0, u, a, ds);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t blk = ((c0 + u) << 6) + lane;
-      if (blk < g.nb) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) block_fma<TYPE, B>(lane, w[r][u], s[r][u], a, ds, u, acc[r]);
-      }
-    }
+    compute(c0, w, s, a, ds);
   }
 
 #pragma unroll
@@ -178,7 +316,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
 // activation blocks (one block per quad of lanes, 8 elements per lane, the
 // qblk_quantize_act arithmetic) into one of two LDS slots; one barrier per
 // chunk publishes them. B activation rows: B blocks per quad per chunk.
-template <int TYPE, int B, int R, bool FUSED>
+template <int TYPE, int B, int R, bool FUSED, bool SYNC = false>
 __global__ __launch_bounds__(256) void gemv_pipe_kernel(GemvArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* s_codes = smem;                                           // [2][B][64*32]
@@ -188,7 +326,12 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(GemvArgs g) {
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
   const int64_t row0 = wave * R;
-  if (!FUSED && row0 >= g.n) return;  // whole wave
+  uint64_t tag = 0;
+  if constexpr (SYNC) {
+    tag = launch_tag();
+    produce<B>(g, tag);
+  }
+  if (!FUSED && !SYNC && row0 >= g.n) return;  // whole wave
   const bool active = row0 < g.n;
   const uint32_t k = g.nb * 32u;
   const uint32_t nchunks = (g.nb + 63u) >> 6;
@@ -271,8 +414,15 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(GemvArgs g) {
   };
 
   issue(0, wa, sa, xa);
+  if constexpr (SYNC) {
+    // both chunk buffers' weight loads are in flight while the activation
+    // is awaited
+    if (1 < nchunks) issue(1, wb, sb, xb);
+    wait_slices<B>(g, tag);
+    if (!active) return;
+  }
   for (uint32_t c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks) issue(c + 1, wb, sb, xb);
+    if (c + 1 < nchunks && !(SYNC && c == 0)) issue(c + 1, wb, sb, xb);
     consume(c, wa, sa, xa);
     if (c + 1 >= nchunks) break;
     if (c + 2 < nchunks) issue(c + 2, wa, sa, xa);
@@ -290,89 +440,111 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(GemvArgs g) {
   }
 }
 
-template <int TYPE, int B, int R, bool FUSED>
-hipError_t launch_pipe(WeightView W, int64_t n, int64_t nb, ActView A, float* y, int64_t ldy,
-                       hipStream_t s, const float* x = nullptr, int64_t ldx = 0) {
-  const int64_t waves = (n + R - 1) / R;
-  const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+// Everything a launch needs besides the kernel variant.
+struct Plan {
+  WeightView W;
+  int64_t n;
+  int64_t nb;
+  ActView A;          // quantized activations (for SYNC: the workspace buffer)
+  float* y;
+  int64_t ldy;
+  const float* x;     // fp32 activations (fused variants)
+  int64_t ldx;
+  uint8_t* work;      // SYNC: workspace (activation buffer, then flags)
+  int64_t flags_off;
+};
+
+inline GemvArgs make_args(const Plan& p) {
   GemvArgs g;
-  g.x = x;
-  g.ldx = ldx;
-  g.w = W.base;
-  g.row_bytes = W.row_bytes;
-  g.hdr_bytes = static_cast<uint32_t>(W.hdr_bytes);
-  g.n = n;
-  g.nb = static_cast<uint32_t>(nb);
-  g.aq = A.q;
-  g.ads = A.ds;
-  g.y = y;
-  g.ldy = ldy;
+  g.x = p.x;
+  g.ldx = p.ldx;
+  g.w = p.W.base;
+  g.row_bytes = p.W.row_bytes;
+  g.hdr_bytes = static_cast<uint32_t>(p.W.hdr_bytes);
+  g.n = p.n;
+  g.nb = static_cast<uint32_t>(p.nb);
+  g.aq = p.A.q;
+  g.ads = p.A.ds;
+  g.y = p.y;
+  g.ldy = p.ldy;
+  g.xq_codes = p.work;
+  g.xq_ds = p.work ? p.work + (p.A.ds - p.A.q) : nullptr;
+  g.flags = p.work ? reinterpret_cast<uint64_t*>(p.work + p.flags_off) : nullptr;
+  g.nslices = static_cast<uint32_t>((p.nb + 63) / 64);
+  g.flag_stride = static_cast<uint32_t>(gemv_flag_stride(p.nb * 32));
+  return g;
+}
+
+template <int R>
+inline dim3 grid_for(int64_t n) {
+  const int64_t waves = (n + R - 1) / R;
+  return dim3(static_cast<uint32_t>((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+}
+
+template <int TYPE, int B, int R, bool FUSED, bool SYNC>
+hipError_t launch_pipe(const Plan& p, hipStream_t s) {
   const size_t shmem = FUSED ? static_cast<size_t>(2 * B * 64 * 40) : 0;
-  hipLaunchKernelGGL((gemv_pipe_kernel<TYPE, B, R, FUSED>), dim3(static_cast<uint32_t>(grid)),
-                     dim3(64 * kWavesPerBlock), shmem, s, g);
+  hipLaunchKernelGGL((gemv_pipe_kernel<TYPE, B, R, FUSED, SYNC>), grid_for<R>(p.n),
+                     dim3(64 * kWavesPerBlock), shmem, s, make_args(p));
   return hipGetLastError();
 }
 
-template <int TYPE, int B, int R, int U>
-hipError_t launch_cfg(WeightView W, int64_t n, int64_t nb, ActView A, float* y, int64_t ldy,
-                      hipStream_t s) {
-  const int64_t waves = (n + R - 1) / R;
-  const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  GemvArgs g;
-  g.x = nullptr;
-  g.ldx = 0;
-  g.w = W.base;
-  g.row_bytes = W.row_bytes;
-  g.hdr_bytes = static_cast<uint32_t>(W.hdr_bytes);
-  g.n = n;
-  g.nb = static_cast<uint32_t>(nb);
-  g.aq = A.q;
-  g.ads = A.ds;
-  g.y = y;
-  g.ldy = ldy;
-  hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U>), dim3(static_cast<uint32_t>(grid)),
-                     dim3(64 * kWavesPerBlock), 0, s, g);
+template <int TYPE, int B, int R, int U, bool SYNC>
+hipError_t launch_cfg(const Plan& p, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U, SYNC>), grid_for<R>(p.n),
+                     dim3(64 * kWavesPerBlock), 0, s, make_args(p));
   return hipGetLastError();
 }
+
+// How the activation reaches the kernel.
+enum Mode { kQuantized = 0, kLdsFused = 1, kInLaunch = 2 };
 
 // Kernel variant per shape, from kernel-trace measurements on MI355X over the
 // 7B- and 70B-shaped Q4_K matrices (batch 1): the classic kernel with 4 rows
 // per wave streams the largest matrices best (6.0-6.3 TB/s), the pipelined
 // kernel with 2 rows per wave the mid-size ones, 1 row per wave with 2 chunks
 // in flight the small ones. All variants give bit-identical results.
-template <int TYPE, int B, bool FUSED = false>
-hipError_t launch_b(WeightView W, int64_t n, int64_t nb, ActView A, float* y, int64_t ldy,
-                    hipStream_t s, const float* x = nullptr, int64_t ldx = 0) {
-  const int64_t k = nb * 32;
-  if constexpr (FUSED) {
-    if (n >= 8192) return launch_pipe<TYPE, B, 4, true>(W, n, nb, A, y, ldy, s, x, ldx);
-    return launch_pipe<TYPE, B, 2, true>(W, n, nb, A, y, ldy, s, x, ldx);
+template <int TYPE, int B, int MODE>
+hipError_t launch_b(const Plan& p, hipStream_t s) {
+  constexpr bool SYNC = MODE == kInLaunch;
+  const int64_t n = p.n, k = p.nb * 32;
+  if constexpr (MODE == kLdsFused) {
+    if (n >= 8192) return launch_pipe<TYPE, B, 4, true, false>(p, s);
+    return launch_pipe<TYPE, B, 2, true, false>(p, s);
   } else if constexpr (B == 1) {
     if (n >= 16384) {
-      if (k >= 8192) return launch_cfg<TYPE, 1, 4, 1>(W, n, nb, A, y, ldy, s);
-      return launch_cfg<TYPE, 1, 2, 1>(W, n, nb, A, y, ldy, s);
+      if (k >= 8192) return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
+      return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
     }
-    if (n >= 8192 && k >= 16384) return launch_cfg<TYPE, 1, 4, 1>(W, n, nb, A, y, ldy, s);
-    if (n >= 3072) return launch_pipe<TYPE, 1, 2, false>(W, n, nb, A, y, ldy, s);
-    return launch_cfg<TYPE, 1, 1, 2>(W, n, nb, A, y, ldy, s);
+    if (n >= 8192 && k >= 16384) return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
+    if (n >= 3072) return launch_pipe<TYPE, 1, 2, false, SYNC>(p, s);
+    return launch_cfg<TYPE, 1, 1, 2, SYNC>(p, s);
   } else {
-    if (n >= 3072) return launch_cfg<TYPE, B, 2, 1>(W, n, nb, A, y, ldy, s);
-    return launch_cfg<TYPE, B, 1, 1>(W, n, nb, A, y, ldy, s);
+    if (n >= 3072) return launch_cfg<TYPE, B, 2, 1, SYNC>(p, s);
+    return launch_cfg<TYPE, B, 1, 1, SYNC>(p, s);
   }
 }
 
-template <int TYPE, bool FUSED = false>
-hipError_t launch_batch(int b, WeightView W, int64_t n, int64_t nb, ActView A, float* y,
-                        int64_t ldy, hipStream_t s, const float* x = nullptr, int64_t ldx = 0) {
+template <int TYPE, int MODE = kQuantized>
+hipError_t launch_batch(int b, const Plan& p, hipStream_t s) {
   switch (b) {
-    case 1: return launch_b<TYPE, 1, FUSED>(W, n, nb, A, y, ldy, s, x, ldx);
-    case 2: return launch_b<TYPE, 2, FUSED>(W, n, nb, A, y, ldy, s, x, ldx);
-    case 3: return launch_b<TYPE, 3, FUSED>(W, n, nb, A, y, ldy, s, x, ldx);
-    case 4: return launch_b<TYPE, 4, FUSED>(W, n, nb, A, y, ldy, s, x, ldx);
-    case 5: return launch_b<TYPE, 5, FUSED>(W, n, nb, A, y, ldy, s, x, ldx);
-    case 6: return launch_b<TYPE, 6, FUSED>(W, n, nb, A, y, ldy, s, x, ldx);
-    case 7: return launch_b<TYPE, 7, FUSED>(W, n, nb, A, y, ldy, s, x, ldx);
-    default: return launch_b<TYPE, 8, FUSED>(W, n, nb, A, y, ldy, s, x, ldx);
+    case 1: return launch_b<TYPE, 1, MODE>(p, s);
+    case 2: return launch_b<TYPE, 2, MODE>(p, s);
+    case 3: return launch_b<TYPE, 3, MODE>(p, s);
+    case 4: return launch_b<TYPE, 4, MODE>(p, s);
+    case 5: return launch_b<TYPE, 5, MODE>(p, s);
+    case 6: return launch_b<TYPE, 6, MODE>(p, s);
+    case 7: return launch_b<TYPE, 7, MODE>(p, s);
+    default: return launch_b<TYPE, 8, MODE>(p, s);
+  }
+}
+
+template <int MODE>
+hipError_t launch_type(int type, int b, const Plan& p, hipStream_t s) {
+  switch (type) {
+    case kQ4_0: return launch_batch<kQ4_0, MODE>(b, p, s);
+    case kQ8_0: return launch_batch<kQ8_0, MODE>(b, p, s);
+    default: return launch_batch<kQ4_K, MODE>(b, p, s);
   }
 }
 
@@ -380,51 +552,56 @@ hipError_t launch_batch(int b, WeightView W, int64_t n, int64_t nb, ActView A, f
 
 hipError_t launch_gemv(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t batch, float* y, int64_t ldy, hipStream_t s) {
-  WeightView W;
-  W.base = static_cast<const uint8_t*>(wq);
-  W.row_bytes = row_bytes(type, k);
-  W.hdr_bytes = header_bytes(type, k);
+  Plan p{};
+  p.W.base = static_cast<const uint8_t*>(wq);
+  p.W.row_bytes = row_bytes(type, k);
+  p.W.hdr_bytes = header_bytes(type, k);
+  p.n = n;
+  p.nb = k / 32;
+  p.ldy = ldy;
   const ActView full = make_act(xq, batch, k);
-  const int64_t nb = k / 32;
   // up to 8 activation rows per launch; the weights are re-streamed for each
   // group of 8 (large batches belong to qblk_gemm)
   for (int64_t b0 = 0; b0 < batch; b0 += 8) {
     const int bc = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
-    ActView A = full;
-    A.q = full.q + b0 * k;
-    A.ds = full.ds + 8 * b0 * nb;
-    float* yb = y + b0 * ldy;
-    hipError_t e;
-    switch (type) {
-      case kQ4_0: e = launch_batch<kQ4_0>(bc, W, n, nb, A, yb, ldy, s); break;
-      case kQ8_0: e = launch_batch<kQ8_0>(bc, W, n, nb, A, yb, ldy, s); break;
-      default: e = launch_batch<kQ4_K>(bc, W, n, nb, A, yb, ldy, s); break;
-    }
+    p.A = full;
+    p.A.q = full.q + b0 * k;
+    p.A.ds = full.ds + 8 * b0 * p.nb;
+    p.y = y + b0 * ldy;
+    const hipError_t e = launch_type<kQuantized>(type, bc, p, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-}  // namespace qblk
-
-namespace qblk {
-
-// Fused quantize + GEMV: fp32 activations in; the caller guarantees that
-// batch <= gemv_f32_max_batch(k), so one launch streams the weights once.
+// Fused quantize + GEMV (fp32 activations, batch <= gemv_f32_max_batch(k)):
+// one launch streams the weights once. Small matrices: every workgroup
+// quantizes the activation into its local memory. Larger ones: the first
+// workgroups quantize it once into the workspace and the others wait for it
+// behind their first weight loads (the per-workgroup quantization would cost
+// more than the weight stream).
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
-                           int64_t ldx, int64_t batch, float* y, int64_t ldy, hipStream_t s) {
-  WeightView W;
-  W.base = static_cast<const uint8_t*>(wq);
-  W.row_bytes = row_bytes(type, k);
-  W.hdr_bytes = header_bytes(type, k);
-  const int64_t nb = k / 32;
-  const ActView none = make_act(nullptr, 0, k);
+                           int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
+                           hipStream_t s) {
+  Plan p{};
+  p.W.base = static_cast<const uint8_t*>(wq);
+  p.W.row_bytes = row_bytes(type, k);
+  p.W.hdr_bytes = header_bytes(type, k);
+  p.n = n;
+  p.nb = k / 32;
+  p.y = y;
+  p.ldy = ldy;
+  p.x = x;
+  p.ldx = ldx;
   const int bc = static_cast<int>(batch);
-  switch (type) {
-    case kQ4_0: return launch_batch<kQ4_0, true>(bc, W, n, nb, none, y, ldy, s, x, ldx);
-    case kQ8_0: return launch_batch<kQ8_0, true>(bc, W, n, nb, none, y, ldy, s, x, ldx);
-    default: return launch_batch<kQ4_K, true>(bc, W, n, nb, none, y, ldy, s, x, ldx);
+  if (n * k <= kLdsFusedMaxElems) {
+    p.A = make_act(nullptr, 0, k);
+    return launch_type<kLdsFused>(type, bc, p, s);
   }
+  p.A = make_act(work, batch, k);
+  p.work = static_cast<uint8_t*>(work);
+  p.flags_off = gemv_flags_offset(batch, k);
+  return launch_type<kInLaunch>(type, bc, p, s);
 }
 
 }  // namespace qblk

@@ -41,11 +41,26 @@ hipError_t launch_pack_weights(int type, const float* w, int64_t n, int64_t k, i
 hipError_t launch_gemv(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t batch, float* y, int64_t ldy, hipStream_t s);
 // Fused quantize + GEMV (fp32 activations): up to 8 activation rows per
-// launch; the kernel keeps two 64-block slices of their codes in LDS
-// (5 KiB per row), so the limit does not depend on k.
+// launch (the local-memory variant keeps two 64-block slices of their codes
+// in LDS, 5 KiB per row, so the limit does not depend on k).
 inline int64_t gemv_f32_max_batch(int64_t k) { return k > 0 ? 8 : 0; }
+// Matrices of at most this many weights quantize the activation in every
+// workgroup's local memory; larger ones quantize it once per launch into the
+// caller's workspace.
+constexpr int64_t kLdsFusedMaxElems = int64_t(32) << 20;
+// Workspace of the in-launch quantization: the activation buffer (same
+// layout as qblk_quantize_act's), then 8 copies of one u64 flag per 64-block
+// slice, each copy padded to whole 128-byte lines.
+inline int64_t gemv_flag_stride(int64_t k) { return ((k / 32 + 63) / 64 + 15) / 16 * 16; }
+inline int64_t gemv_flags_offset(int64_t batch, int64_t k) {
+  return (batch * k + 8 * batch * (k / 32) + 255) / 256 * 256;
+}
+inline int64_t gemv_f32_work_bytes(int64_t batch, int64_t k) {
+  return gemv_flags_offset(batch, k) + 8 * 8 * gemv_flag_stride(k);
+}
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
-                           int64_t ldx, int64_t batch, float* y, int64_t ldy, hipStream_t s);
+                           int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
+                           hipStream_t s);
 hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t m, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,

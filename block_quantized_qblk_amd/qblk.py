@@ -47,7 +47,8 @@ def _load():
         "qblk_gemv": (i32, [i32, vp, i64, i64, vp, i64, vp, i64, vp]),
         "qblk_gemm": (i32, [i32, vp, i64, i64, vp, i64, vp, i64, vp]),
         "qblk_gemv_f32_max_batch": (i32, [i64]),
-        "qblk_gemv_f32": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]),
+        "qblk_gemv_f32_work_bytes": (ctypes.c_size_t, [i64, i64]),
+        "qblk_gemv_f32": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp, vp]),
         "qblk_block_sums": (i32, [i32, vp, i64, i64, vp, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -181,9 +182,15 @@ def qblk_gemv_f32_max_batch(k):
     return int(_load().qblk_gemv_f32_max_batch(int(k)))
 
 
-def qblk_gemv_f32(wtype, wq, n, k, x, batch=None, y=None, stream=None):
+def qblk_gemv_f32_work_bytes(batch, k):
+    return int(_load().qblk_gemv_f32_work_bytes(int(batch), int(k)))
+
+
+def qblk_gemv_f32(wtype, wq, n, k, x, batch=None, y=None, work=None, stream=None):
     """y[b, :n] = W quant(x_b): activation quantization fused into the GEMV.
-    x: float32 [batch, >= k] device tensor with unit stride along rows."""
+    x: float32 [batch, >= k] device tensor with unit stride along rows.
+    work: uint8 device workspace of qblk_gemv_f32_work_bytes(batch, k) bytes
+    (allocated here when None); calls that may overlap need their own."""
     import torch
     _require_cuda(wq, "wq")
     _require_cuda(x, "x", rows=True)
@@ -198,8 +205,14 @@ def qblk_gemv_f32(wtype, wq, n, k, x, batch=None, y=None, stream=None):
         raise ValueError("y must be float32 [batch, >= n]")
     if wq.numel() < qblk_weight_bytes(wtype, n, k):
         raise ValueError("wq smaller than the packed size")
+    need = qblk_gemv_f32_work_bytes(batch, k)
+    if work is None:
+        work = torch.empty(max(need, 1), dtype=torch.uint8, device=wq.device)
+    _require_cuda(work, "work")
+    if work.numel() < need:
+        raise ValueError("work smaller than qblk_gemv_f32_work_bytes(batch, k)")
     _check(_load().qblk_gemv_f32(_type(wtype), _ptr(wq), int(n), int(k), _ptr(x), x.stride(0),
-                                 int(batch), _ptr(y), y.stride(0), _stream(stream)),
+                                 int(batch), _ptr(y), y.stride(0), _ptr(work), _stream(stream)),
            "qblk_gemv_f32")
     return y
 

@@ -160,22 +160,33 @@ int qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void *xq,
 
 /*
  * Decode-path product with the activation quantization fused in: the same
- * result, bit for bit, as qblk_quantize_act(x) followed by qblk_gemv, but in
- * one launch and without the activation buffer. Each workgroup quantizes
- * the fp32 rows, 64 blocks at a time, into its local memory with the
- * qblk_quantize_act rule ("llama.cpp 推理引擎", §5.1 at 8 bits) while it
- * streams its weight rows. Every workgroup repeats the quantization, so this
- * saves time over the two-step path only for small matrices (measured on
- * MI355X: up to about 4096 x 4096).
- *   x : fp32 [batch][ldx];  other arguments as qblk_gemv.
+ * result, bit for bit, as qblk_quantize_act(x) followed by qblk_gemv, in one
+ * launch. The activation is quantized with the qblk_quantize_act rule
+ * ("llama.cpp 推理引擎", §5.1 at 8 bits):
+ *   - matrices of at most 32M weights: every workgroup quantizes the fp32
+ *     rows, 64 blocks at a time, into its local memory while it streams its
+ *     weight rows (work is not touched);
+ *   - larger ones: the first workgroups of the launch quantize the rows once
+ *     into `work` and publish each 64-block slice with a tag unique to the
+ *     launch; the other workgroups issue their first weight loads, then wait
+ *     for the tags (a bounded wait: past about 20 ms a workgroup quantizes
+ *     the rows itself, so the result never depends on scheduling).
+ *   x    : fp32 [batch][ldx];  other arguments as qblk_gemv.
+ *   work : device workspace of qblk_gemv_f32_work_bytes(batch, k) bytes,
+ *          256-byte aligned, owned by the caller. It holds no state that a
+ *          later call depends on (it need not be cleared), but calls that
+ *          may run at the same time must use different workspaces.
  * batch <= qblk_gemv_f32_max_batch(k) (8 for any valid k, 0 when k is
  * invalid).
- * Errors: as qblk_gemv, plus QBLK_ERR_SHAPE for ldx < k, QBLK_ERR_ALIGN for x
- * or ldx, QBLK_ERR_UNSUPPORTED for batch > qblk_gemv_f32_max_batch(k).
+ * Errors: as qblk_gemv, plus QBLK_ERR_SHAPE for ldx < k, QBLK_ERR_ARG for a
+ * null work, QBLK_ERR_ALIGN for x, ldx or work, QBLK_ERR_UNSUPPORTED for
+ * batch > qblk_gemv_f32_max_batch(k).
  */
 int qblk_gemv_f32_max_batch(int64_t k);
+size_t qblk_gemv_f32_work_bytes(int64_t batch, int64_t k); /* 0 if invalid */
 int qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const float *x,
-                  int64_t ldx, int64_t batch, float *y, int64_t ldy, hipStream_t stream);
+                  int64_t ldx, int64_t batch, float *y, int64_t ldy, void *work,
+                  hipStream_t stream);
 
 /*
  * Prefill-path product: the same result as qblk_gemv for m activation rows,

@@ -129,3 +129,26 @@ def test_quantize_and_pack_argument_validation():
     b = lib.qblk_block_sums
     assert b(3, x, 4, 256, xq, 2, NULL, NULL) == ERR_ARG
     assert b(3, x, 4, 200, xq, 2, _p(FAKE), NULL) == ERR_SHAPE
+
+
+def test_gemv_f32_workspace_size_and_validation():
+    for k in (32, 2048, 4096, 8192, 28672, 1 << 20):
+        for b in (1, 4, 8):
+            wb = qblk.qblk_gemv_f32_work_bytes(b, k)
+            # the activation buffer plus 8 copies of one 8-byte flag per 64 blocks
+            assert wb >= o.act_bytes(b, k) + 8 * 8 * (-(-k // 2048))
+            assert wb % 256 == 0
+    assert qblk.qblk_gemv_f32_work_bytes(9, 4096) == 0
+    assert qblk.qblk_gemv_f32_work_bytes(1, 100) == 0
+    assert qblk.qblk_gemv_f32_work_bytes(-1, 4096) == 0
+    lib = qblk.lib()
+    f = lib.qblk_gemv_f32
+    w, x, y, wk = _p(FAKE), _p(FAKE + 0x100000), _p(FAKE + 0x200000), _p(FAKE + 0x300000)
+    assert f(3, w, 16, 256, x, 256, 1, y, 16, NULL, NULL) == ERR_ARG            # null work
+    assert f(3, w, 16, 256, x, 256, 1, y, 16, _p(FAKE + 0x300010), NULL) == ERR_ALIGN
+    assert f(3, w, 16, 256, x, 255, 1, y, 16, wk, NULL) == ERR_SHAPE            # ldx < k
+    assert f(3, w, 16, 256, x, 258, 1, y, 16, wk, NULL) == ERR_ALIGN            # ldx % 4
+    assert f(3, w, 16, 256, _p(FAKE + 4), 256, 1, y, 16, wk, NULL) == ERR_ALIGN
+    assert f(3, w, 16, 256, x, 256, 9, y, 16, wk, NULL) == ERR_UNSUPPORTED      # batch > 8
+    assert f(3, w, 16, 288, x, 288, 1, y, 16, wk, NULL) == ERR_SHAPE
+    assert f(3, NULL, 0, 256, NULL, 256, 1, NULL, 0, NULL, NULL) == OK          # empty

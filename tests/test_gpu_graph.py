@@ -51,3 +51,32 @@ def test_graph_replays_match_eager():
         assert t.equal(xq, refq), rep
         assert t.equal(y1, ref1), rep
         assert t.equal(y2, ref2), rep
+
+
+def test_graph_replays_fused_gemv_in_launch_quantization():
+    """qblk_gemv_f32 on a matrix that takes the in-launch quantization path,
+    captured once: each replay reads the activation that is in x at replay
+    time (new values are written between replays), and must equal quantize +
+    GEMV run eagerly on those values."""
+    print("graph capture: gemv_f32 with in-launch quantization", flush=True)
+    t = torch()
+    n, k = 17000, 4096
+    w = synth.weights(3, 6, n, k)
+    wq = qblk.qblk_pack_weights(qblk.Q4_K, dev(w))
+    x = dev(synth.act(3, 1, k))
+    y = t.empty((1, n), dtype=t.float32, device="cuda")
+    work = t.zeros(qblk.qblk_gemv_f32_work_bytes(1, k), dtype=t.uint8, device="cuda")
+    qblk.qblk_gemv_f32(qblk.Q4_K, wq, n, k, x, y=y, work=work)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        qblk.qblk_gemv_f32(qblk.Q4_K, wq, n, k, x, y=y, work=work)
+    for rep in range(5):
+        x.copy_(dev(synth.act(3, 1, k, index=90 - rep)))
+        y.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        ref = qblk.qblk_gemv(qblk.Q4_K, wq, n, k, qblk.qblk_quantize_act(x), 1)
+        t.cuda.synchronize()
+        assert t.equal(y, ref), rep

@@ -328,6 +328,36 @@ def test_gemv_f32_matches_quantize_then_gemv(wtype, n, k, batch):
         check_rel(fused[:, rows], expected(wtype, w[rows], x))
 
 
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("n,k,batch", [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1),
+                                       (9000, 4096, 4), (3, 1 << 24, 1)])
+def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
+    """Matrices above 32M weights quantize the activation once per launch
+    into the workspace. One workspace serves consecutive calls on different
+    activations (a stale slice would reproduce the previous call's result),
+    also when it starts out holding arbitrary bytes; the (3, 2^24) case has
+    fewer workgroups than activation slices."""
+    t = torch()
+    print(f"gemv_f32 in-launch {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
+    assert n * k > 32 << 20
+    rng = np.random.default_rng(5 * wtype + n + k)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    wq = dev_pack(wtype, w)
+    work = t.randint(0, 256, (qblk.qblk_gemv_f32_work_bytes(batch, k),), dtype=t.uint8,
+                     device="cuda")
+    for call in range(3):
+        x = rng.standard_normal((batch, k)).astype(np.float32)
+        if call == 1:
+            x *= np.float32(1e-3)
+        xd = dev(x)
+        fused = host(qblk.qblk_gemv_f32(wtype, wq, n, k, xd, work=work))
+        two_step = host(qblk.qblk_gemv(wtype, wq, n, k, qblk.qblk_quantize_act(xd), batch))
+        assert np.array_equal(fused.view(np.uint32), two_step.view(np.uint32)), call
+    if k <= 28672:
+        rows = _sample_rows(n, 16, n)
+        check_rel(fused[:, rows], expected(wtype, w[rows], x))
+
+
 def test_gemv_f32_strided_rows_and_limits():
     print("gemv_f32 strided x / limits", flush=True)
     rng = np.random.default_rng(8)
