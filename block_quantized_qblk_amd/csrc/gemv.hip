@@ -201,12 +201,68 @@ __device__ __forceinline__ void block_fma(uint32_t lane, const WChunk<TYPE>& w,
   }
 }
 
+// ---------------------------------------------------------------- activation staging
+// A workgroup copies the B rows' activation buffer into LDS once, so the
+// waves read their 40 bytes per block and row from LDS rather than from L2
+// for every group of R rows. LDS layout per activation row (stride
+// act_lds_row(nb), whole 2 KiB chunks): for chunk c, the first 16 code bytes
+// of its 64 blocks, then the second 16 (a lane's 16-B read is then
+// contiguous with its neighbours', free of bank conflicts); after the B rows
+// of codes the (d, sum) pairs, [B][nb].
+__host__ __device__ inline uint32_t act_lds_row(uint32_t nb) { return ((nb + 63u) >> 6) * 2048u; }
+__host__ __device__ inline uint32_t act_lds_bytes(int b, uint32_t nb) {
+  return static_cast<uint32_t>(b) * (act_lds_row(nb) + 8u * nb);
+}
+// LDS bytes per workgroup up to which the activations are staged
+constexpr uint32_t kActLdsMax = 16384;
+
+template <int B>
+__device__ __forceinline__ void stage_acts(const GemvArgs& g, uint8_t* smem) {
+  const uint32_t k = g.nb * 32u, kp = act_lds_row(g.nb);
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    for (uint32_t u = threadIdx.x; u < k / 16u; u += 256u) {
+      const uint32_t blk = u >> 1, h = u & 1u;
+      *reinterpret_cast<uint4*>(smem + b * kp + (((blk >> 6) * 2u + h) << 10) + ((blk & 63u) << 4)) =
+          load16(g.aq + b * k + 16u * u);
+    }
+  }
+  uint8_t* sds = smem + B * kp;
+  for (uint32_t i = threadIdx.x; i < B * g.nb; i += 256u)
+    *reinterpret_cast<uint2*>(sds + 8u * i) = *reinterpret_cast<const uint2*>(g.ads + 8u * i);
+}
+
+// One lane's activation data of block `blk` for the B rows, from LDS
+// (ALDS) or from the global activation buffer.
+template <int B, int U, bool ALDS>
+__device__ __forceinline__ void load_act_block(const GemvArgs& g, const uint8_t* smem, uint32_t blk,
+                                               int u, uint4 (&a)[B][U][2], float2 (&ds)[B][U]) {
+  const uint32_t k = g.nb * 32u;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    if constexpr (ALDS) {
+      const uint8_t* ap = smem + b * act_lds_row(g.nb) + (((blk >> 6) * 2u) << 10) + ((blk & 63u) << 4);
+      a[b][u][0] = *reinterpret_cast<const uint4*>(ap);
+      a[b][u][1] = *reinterpret_cast<const uint4*>(ap + 1024);
+      ds[b][u] = *reinterpret_cast<const float2*>(smem + B * act_lds_row(g.nb) + 8u * (b * g.nb + blk));
+    } else {
+      const uint8_t* ap = g.aq + b * k;
+      a[b][u][0] = load16(ap + 32u * blk);
+      a[b][u][1] = load16(ap + (32u * blk + 16u));
+      ds[b][u] = *reinterpret_cast<const float2*>(g.ads + 8u * (b * g.nb) + 8u * blk);
+    }
+  }
+}
+
 // Classic variant: each wave issues the loads of U chunks for its R rows,
 // then computes them; occupancy hides the latency. Best for large matrices.
 // SYNC: the activation is quantized inside the launch (produce /
-// wait_slices); the first chunks' weight loads are issued before the wait.
-template <int TYPE, int B, int R, int U, bool SYNC = false>
+// wait_slices); ALDS: it is read from LDS (stage_acts). Either way the first
+// chunks' weight loads are issued before the wait / staging.
+template <int TYPE, int B, int R, int U, bool SYNC = false, bool ALDS = false>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr bool kAllWaves = SYNC || ALDS;  // workgroup barriers ahead: no early exit
   const uint32_t lane = threadIdx.x & 63;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -215,10 +271,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
   if constexpr (SYNC) {
     tag = launch_tag();
     produce<B>(g, tag);
-  } else {
+  }
+  if constexpr (!kAllWaves) {
     if (row0 >= g.n) return;  // whole wave
   }
-  const bool active = !SYNC || row0 < g.n;  // SYNC: every wave takes part in the waits
+  const bool active = !kAllWaves || row0 < g.n;
   const uint8_t* wrow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -246,15 +303,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
   };
   auto load_acts = [&](uint32_t c0, int u, uint4(&a)[B][U][2], float2(&ds)[B][U]) {
     const uint32_t blk = ((c0 + u) << 6) + lane;
-    if (blk < g.nb) {
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const uint8_t* ap = g.aq + b * k;
-        a[b][u][0] = load16(ap + 32u * blk);
-        a[b][u][1] = load16(ap + (32u * blk + 16u));
-        ds[b][u] = *reinterpret_cast<const float2*>(g.ads + 8u * (b * g.nb) + 8u * blk);
-      }
-    }
+    if (blk < g.nb) load_act_block<B, U, ALDS>(g, smem, blk, u, a, ds);
   };
   auto compute = [&](uint32_t c0, const WChunk<TYPE>(&w)[R][U], const WScale<TYPE>(&s)[R][U],
                      const uint4(&a)[B][U][2], const float2(&ds)[B][U]) {
@@ -269,12 +318,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
   };
 
   uint32_t c_start = 0;
-  if constexpr (SYNC) {
-    // first U chunks: weight loads in flight while the activation is awaited
+  if constexpr (kAllWaves) {
+    // first U chunks: weight loads in flight while the activation is
+    // awaited / staged
     WChunk<TYPE> w[R][U];
     WScale<TYPE> s[R][U];
     load_weights(0, w, s);
-    wait_slices<B>(g, tag);
+    if constexpr (SYNC) wait_slices<B>(g, tag);
+    if constexpr (ALDS) {
+      stage_acts<B>(g, smem);
+      __syncthreads();
+    }
     if (!active) return;
     uint4 a[B][U][2];
     float2 ds[B][U];
@@ -316,7 +370,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
 // activation blocks (one block per quad of lanes, 8 elements per lane, the
 // qblk_quantize_act arithmetic) into one of two LDS slots; one barrier per
 // chunk publishes them. B activation rows: B blocks per quad per chunk.
-template <int TYPE, int B, int R, bool FUSED, bool SYNC = false>
+template <int TYPE, int B, int R, bool FUSED, bool SYNC = false, bool ALDS = false>
 __global__ __launch_bounds__(256) void gemv_pipe_kernel(GemvArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* s_codes = smem;                                           // [2][B][64*32]
@@ -331,7 +385,7 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(GemvArgs g) {
     tag = launch_tag();
     produce<B>(g, tag);
   }
-  if (!FUSED && !SYNC && row0 >= g.n) return;  // whole wave
+  if (!FUSED && !SYNC && !ALDS && row0 >= g.n) return;  // whole wave
   const bool active = row0 < g.n;
   const uint32_t k = g.nb * 32u;
   const uint32_t nchunks = (g.nb + 63u) >> 6;
@@ -402,27 +456,27 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(GemvArgs g) {
         a[b][0][0] = *reinterpret_cast<const uint4*>(ap);
         a[b][0][1] = *reinterpret_cast<const uint4*>(ap + 16);
         ds[b][0] = s_ds[(slot * B + b) * 64u + lane];
-      } else {
-        const uint8_t* ap = g.aq + b * k;
-        a[b][0][0] = load16(ap + 32u * blk);
-        a[b][0][1] = load16(ap + (32u * blk + 16u));
-        ds[b][0] = *reinterpret_cast<const float2*>(g.ads + 8u * (b * g.nb) + 8u * blk);
       }
     }
+    if constexpr (!FUSED) load_act_block<B, 1, ALDS>(g, smem, blk, 0, a, ds);
 #pragma unroll
     for (int r = 0; r < R; ++r) block_fma<TYPE, B>(lane, w[r], s[r], a, ds, 0, acc[r]);
   };
 
   issue(0, wa, sa, xa);
-  if constexpr (SYNC) {
+  if constexpr (SYNC || ALDS) {
     // both chunk buffers' weight loads are in flight while the activation
-    // is awaited
+    // is awaited / staged
     if (1 < nchunks) issue(1, wb, sb, xb);
-    wait_slices<B>(g, tag);
+    if constexpr (SYNC) wait_slices<B>(g, tag);
+    if constexpr (ALDS) {
+      stage_acts<B>(g, smem);
+      __syncthreads();
+    }
     if (!active) return;
   }
   for (uint32_t c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks && !(SYNC && c == 0)) issue(c + 1, wb, sb, xb);
+    if (c + 1 < nchunks && !((SYNC || ALDS) && c == 0)) issue(c + 1, wb, sb, xb);
     consume(c, wa, sa, xa);
     if (c + 1 >= nchunks) break;
     if (c + 2 < nchunks) issue(c + 2, wa, sa, xa);
@@ -481,29 +535,47 @@ inline dim3 grid_for(int64_t n) {
   return dim3(static_cast<uint32_t>((waves + kWavesPerBlock - 1) / kWavesPerBlock));
 }
 
+// The activation rows are staged in LDS when they fit kActLdsMax.
+inline bool stage_in_lds(int b, int64_t nb) {
+  return act_lds_bytes(b, static_cast<uint32_t>(nb)) <= kActLdsMax;
+}
+
 template <int TYPE, int B, int R, bool FUSED, bool SYNC>
 hipError_t launch_pipe(const Plan& p, hipStream_t s) {
-  const size_t shmem = FUSED ? static_cast<size_t>(2 * B * 64 * 40) : 0;
-  hipLaunchKernelGGL((gemv_pipe_kernel<TYPE, B, R, FUSED, SYNC>), grid_for<R>(p.n),
-                     dim3(64 * kWavesPerBlock), shmem, s, make_args(p));
+  if (!FUSED && stage_in_lds(B, p.nb)) {
+    hipLaunchKernelGGL((gemv_pipe_kernel<TYPE, B, R, false, SYNC, true>), grid_for<R>(p.n),
+                       dim3(64 * kWavesPerBlock), act_lds_bytes(B, static_cast<uint32_t>(p.nb)),
+                       s, make_args(p));
+  } else {
+    const size_t shmem = FUSED ? static_cast<size_t>(2 * B * 64 * 40) : 0;
+    hipLaunchKernelGGL((gemv_pipe_kernel<TYPE, B, R, FUSED, SYNC, false>), grid_for<R>(p.n),
+                       dim3(64 * kWavesPerBlock), shmem, s, make_args(p));
+  }
   return hipGetLastError();
 }
 
 template <int TYPE, int B, int R, int U, bool SYNC>
 hipError_t launch_cfg(const Plan& p, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U, SYNC>), grid_for<R>(p.n),
-                     dim3(64 * kWavesPerBlock), 0, s, make_args(p));
+  if (stage_in_lds(B, p.nb)) {
+    hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U, SYNC, true>), grid_for<R>(p.n),
+                       dim3(64 * kWavesPerBlock), act_lds_bytes(B, static_cast<uint32_t>(p.nb)),
+                       s, make_args(p));
+  } else {
+    hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U, SYNC, false>), grid_for<R>(p.n),
+                       dim3(64 * kWavesPerBlock), 0, s, make_args(p));
+  }
   return hipGetLastError();
 }
 
 // How the activation reaches the kernel.
 enum Mode { kQuantized = 0, kLdsFused = 1, kInLaunch = 2 };
 
-// Kernel variant per shape, from kernel-trace measurements on MI355X over the
-// 7B- and 70B-shaped Q4_K matrices (batch 1): the classic kernel with 4 rows
-// per wave streams the largest matrices best (6.0-6.3 TB/s), the pipelined
-// kernel with 2 rows per wave the mid-size ones, 1 row per wave with 2 chunks
-// in flight the small ones. All variants give bit-identical results.
+// Kernel variant per shape, from measurements on MI355X over the 7B- and
+// 70B-shaped Q4_K matrices (batch 1, graphs of back-to-back launches): the
+// classic kernel with 4 rows per wave streams the largest matrices best
+// (6.0-6.5 TB/s), with 2 rows per wave the mid-size ones (activations staged
+// in LDS), 1 row per wave with 2 chunks in flight the small ones. All
+// variants give bit-identical results.
 template <int TYPE, int B, int MODE>
 hipError_t launch_b(const Plan& p, hipStream_t s) {
   constexpr bool SYNC = MODE == kInLaunch;
@@ -517,7 +589,7 @@ hipError_t launch_b(const Plan& p, hipStream_t s) {
       return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
     }
     if (n >= 8192 && k >= 16384) return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
-    if (n >= 3072) return launch_pipe<TYPE, 1, 2, false, SYNC>(p, s);
+    if (n >= 3072) return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
     return launch_cfg<TYPE, 1, 1, 2, SYNC>(p, s);
   } else {
     if (n >= 3072) return launch_cfg<TYPE, B, 2, 1, SYNC>(p, s);
