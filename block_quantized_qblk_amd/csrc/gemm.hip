@@ -34,6 +34,8 @@
 // 4-bit weights are unpacked in registers to the same 0,2,4,6,1,3,5,7 order
 // the activation codes are stored in, so A and B slots pair up element by
 // element without byte permutes.
+#include <type_traits>
+
 #include "qblk_device.h"
 
 namespace qblk {
@@ -50,10 +52,19 @@ constexpr int kThreads = 256;  // 4 waves, 2 x 2, each 64 x 64
 constexpr int kMagicBits = 0x4B400000;  // fp32 1.5 * 2^23
 constexpr float kMagic = 12582912.0f;
 
+// Min-term operands of a step in LDS (Q4_K: d_act * code sum and d_min * mn;
+// Q4_0: d_act * code sum and -8 d); Q8_0 has no min term.
+struct MinOps {
+  float asc[KB][BM];  // d * (code sum)
+  float wm[KB][BN];   // weight block min
+};
+struct NoMinOps {};
+
 template <int TYPE>
 struct Cfg {
   static constexpr int kWRow = TYPE == kQ8_0 ? 32 * KB : 16 * KB;  // weight bytes per row per step
   static constexpr bool kHasMin = TYPE != kQ8_0;
+  using Min = std::conditional_t<kHasMin, MinOps, NoMinOps>;
 };
 
 // One LDS buffer: the codes of a K step (filled by direct loads) and its
@@ -63,9 +74,9 @@ struct Stage {
   uint8_t a[BM * 32 * KB];       // activation codes, row r at 128 r, swizzled
   uint8_t w[BN * Cfg<TYPE>::kWRow];  // weight codes, row r at kWRow r, swizzled
   float sa[KB][BM];              // activation scale d
-  float asc[KB][BM];             // d * (code sum)
   float sw[KB][BN];              // weight block scale
-  float wm[KB][BN];              // weight block min (Q4_K, Q4_0)
+  typename Cfg<TYPE>::Min mn;    // min-term operands (not for Q8_0: keeps its two
+                                 // stages within half the CU's LDS)
 };
 
 // 16-byte unit positions inside a row (XOR swizzle)
@@ -168,9 +179,11 @@ __device__ __forceinline__ void store_scales(Stage<TYPE>* __restrict__ S, const 
   const int h = tid & 1;
   const float d0 = __uint_as_float(s.act.x), d1 = __uint_as_float(s.act.z);
   S->sa[2 * h][r] = d0;
-  S->asc[2 * h][r] = d0 * static_cast<float>(static_cast<int>(s.act.y));
   S->sa[2 * h + 1][r] = d1;
-  S->asc[2 * h + 1][r] = d1 * static_cast<float>(static_cast<int>(s.act.w));
+  if constexpr (Cfg<TYPE>::kHasMin) {
+    S->mn.asc[2 * h][r] = d0 * static_cast<float>(static_cast<int>(s.act.y));
+    S->mn.asc[2 * h + 1][r] = d1 * static_cast<float>(static_cast<int>(s.act.w));
+  }
   if (tid < BN) {
     if constexpr (TYPE == kQ4_K) {
       const float d = half_bits_to_float(s.wgt.x);
@@ -179,7 +192,7 @@ __device__ __forceinline__ void store_scales(Stage<TYPE>* __restrict__ S, const 
 #pragma unroll
       for (int jj = 0; jj < KB; ++jj) {
         S->sw[jj][tid] = d * static_cast<float>(q4k_sc(s.wgt, j0 + jj));
-        S->wm[jj][tid] = dmin * static_cast<float>(q4k_mn(s.wgt, j0 + jj));
+        S->mn.wm[jj][tid] = dmin * static_cast<float>(q4k_mn(s.wgt, j0 + jj));
       }
     } else {
       const float dw[4] = {__uint_as_float(s.wgt.x), __uint_as_float(s.wgt.y),
@@ -187,7 +200,7 @@ __device__ __forceinline__ void store_scales(Stage<TYPE>* __restrict__ S, const 
 #pragma unroll
       for (int jj = 0; jj < KB; ++jj) {
         S->sw[jj][tid] = dw[jj];
-        S->wm[jj][tid] = -8.0f * dw[jj];  // Q4_0: codes are nibble - 8
+        if constexpr (Cfg<TYPE>::kHasMin) S->mn.wm[jj][tid] = -8.0f * dw[jj];  // Q4_0: nibble - 8
       }
     }
   }
@@ -264,9 +277,9 @@ __device__ __forceinline__ void compute(const Stage<TYPE>* __restrict__ S, int n
         const bool okb = b < nblk;
         float af[2], bf[2];
 #pragma unroll
-        for (int tm = 0; tm < 2; ++tm) af[tm] = okb ? S->asc[b][wm0 + 32 * tm + l32] : 0.0f;
+        for (int tm = 0; tm < 2; ++tm) af[tm] = okb ? S->mn.asc[b][wm0 + 32 * tm + l32] : 0.0f;
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) bf[tn] = okb ? S->wm[b][wn0 + 32 * tn + l32] : 0.0f;
+        for (int tn = 0; tn < 2; ++tn) bf[tn] = okb ? S->mn.wm[b][wn0 + 32 * tn + l32] : 0.0f;
 #pragma unroll
         for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
