@@ -80,7 +80,7 @@ struct Stage {
 };
 
 // 16-byte unit positions inside a row (XOR swizzle)
-__device__ __forceinline__ int a_pos(int r, int c) { return c ^ (r & 7); }  // 8 units per row
+__device__ __forceinline__ int a_pos(int r, int c) { return c ^ ((r >> 1) & 7); }  // 8 units per row
 template <int TYPE>
 __device__ __forceinline__ int w_pos(int r, int c) {
   if constexpr (TYPE == kQ8_0) return c ^ (r & 7);  // 8 units per row
@@ -100,41 +100,68 @@ struct GemmCtx {
   int64_t n, nb, m, m0, n0;
 };
 
+// Per-lane sources of the direct loads, fixed for the launch: 32-bit byte
+// offsets from the tile's first activation row / weight row (whose 64-bit
+// addresses are wave-uniform), and the 16-byte unit of the step each load
+// fills (a load is skipped when its unit lies past the last block).
+template <int TYPE>
+struct DmaLanes {
+  static constexpr int kUnits = Cfg<TYPE>::kWRow / 16;  // weight units per row
+  static constexpr int kInstr = BN * kUnits / 64 / 4;   // weight loads per wave
+  const uint8_t* a_base;
+  const uint8_t* w_base;
+  uint32_t a_off[4];
+  uint32_t w_off[kInstr];
+  int a_unit[4];
+  int w_unit[kInstr];
+};
+
+template <int TYPE>
+__device__ __forceinline__ DmaLanes<TYPE> dma_lanes(const GemmCtx<TYPE>& g, int wave, int lane) {
+  DmaLanes<TYPE> d;
+  const int64_t k = g.nb * 32;
+  d.a_base = g.A.q + g.m0 * k;
+  d.w_base = g.W.base + g.n0 * g.W.row_bytes + g.W.hdr_bytes;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = 64 * (4 * wave + i) + lane;  // unit index in the stage
+    const int r = u >> 3;
+    d.a_unit[i] = a_pos(r, u & 7);  // global unit stored at this position
+    const int64_t rr = g.m0 + r < g.m ? r : g.m - 1 - g.m0;
+    d.a_off[i] = static_cast<uint32_t>(rr * k + 16 * d.a_unit[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < DmaLanes<TYPE>::kInstr; ++i) {
+    const int u = 64 * (DmaLanes<TYPE>::kInstr * wave + i) + lane;
+    const int r = u / DmaLanes<TYPE>::kUnits;
+    d.w_unit[i] = w_pos<TYPE>(r, u % DmaLanes<TYPE>::kUnits);
+    const int64_t rr = g.n0 + r < g.n ? r : g.n - 1 - g.n0;
+    d.w_off[i] = static_cast<uint32_t>(rr * g.W.row_bytes + 16 * d.w_unit[i]);
+  }
+  return d;
+}
+
 // Direct global-to-LDS loads of step `st`'s codes into stage `S` (issued by
 // every wave; each wave instruction writes 1 KiB of the stage).
 template <int TYPE>
-__device__ __forceinline__ void issue_codes(const GemmCtx<TYPE>& g, Stage<TYPE>* __restrict__ S, int64_t st,
-                                            int wave, int lane) {
+__device__ __forceinline__ void issue_codes(const GemmCtx<TYPE>& g, const DmaLanes<TYPE>& d,
+                                            Stage<TYPE>* __restrict__ S, int64_t st, int wave) {
   const int64_t blk0 = st * KB;
   const int nblk = static_cast<int>(g.nb - blk0 < KB ? g.nb - blk0 : KB);
+  const uint32_t a_step = static_cast<uint32_t>(32 * blk0);
+  const uint32_t w_step = static_cast<uint32_t>((Cfg<TYPE>::kWRow / KB) * blk0);
   // activations: BM rows x 8 units = 16 instructions, 4 per wave
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int I = 4 * wave + i;
-    const int u = 64 * I + lane;  // unit index in the stage
-    const int r = u >> 3;
-    const int c = a_pos(r, u & 7);  // global unit stored at this position
-    const int64_t gm = g.m0 + r < g.m ? g.m0 + r : g.m - 1;
-    if (c < 2 * nblk) {
-      lds_dma16(g.A.codes(gm, blk0) + 16 * c, S->a + 1024 * I);
-    }
+    if (d.a_unit[i] < 2 * nblk) lds_dma16(d.a_base + (d.a_off[i] + a_step), S->a + 1024 * (4 * wave + i));
   }
   // weights
-  constexpr int kUnits = Cfg<TYPE>::kWRow / 16;       // units per row
-  constexpr int kInstr = BN * kUnits / 64 / 4;        // per wave
-  constexpr int kPerBlk = kUnits / KB;                // units per block (1 or 2)
+  constexpr int kPerBlk = DmaLanes<TYPE>::kUnits / KB;  // units per block (1 or 2)
 #pragma unroll
-  for (int i = 0; i < kInstr; ++i) {
-    const int I = kInstr * wave + i;
-    const int u = 64 * I + lane;
-    const int r = u / kUnits;
-    const int c = w_pos<TYPE>(r, u % kUnits);
-    const int64_t gn = g.n0 + r < g.n ? g.n0 + r : g.n - 1;
-    if (c < kPerBlk * nblk) {
-      const uint8_t* src =
-          g.W.row(gn) + g.W.hdr_bytes + (Cfg<TYPE>::kWRow / KB) * blk0 + 16 * c;
-      lds_dma16(src, S->w + 1024 * I);
-    }
+  for (int i = 0; i < DmaLanes<TYPE>::kInstr; ++i) {
+    if (d.w_unit[i] < kPerBlk * nblk)
+      lds_dma16(d.w_base + (d.w_off[i] + w_step),
+                S->w + 1024 * (DmaLanes<TYPE>::kInstr * wave + i));
   }
 }
 
@@ -144,29 +171,46 @@ struct ScaleRegs {
   uint4 wgt;  // Q4_K header / four fp32 block scales of one weight row
 };
 
+// Per-thread scale sources, fixed for the launch: the (d, sum) pairs of
+// blocks 2h, 2h+1 of activation row tid/2, and weight row tid's header /
+// scale region (threads below BN).
+struct ScaleLanes {
+  const uint8_t* act;
+  const uint8_t* wgt;
+};
+
 template <int TYPE>
-__device__ __forceinline__ ScaleRegs load_scales(const GemmCtx<TYPE>& g, int64_t st, int tid) {
+__device__ __forceinline__ ScaleLanes scale_lanes(const GemmCtx<TYPE>& g, int tid) {
+  ScaleLanes l;
+  const int r = tid >> 1, h = tid & 1;
+  const int64_t gm = g.m0 + r < g.m ? g.m0 + r : g.m - 1;
+  l.act = g.A.ds + 8 * (gm * g.nb + 2 * h);
+  const int64_t gn = g.n0 + (tid & (BN - 1)) < g.n ? g.n0 + (tid & (BN - 1)) : g.n - 1;
+  l.wgt = g.W.row(gn);
+  return l;
+}
+
+template <int TYPE>
+__device__ __forceinline__ ScaleRegs load_scales(const GemmCtx<TYPE>& g, const ScaleLanes& sl,
+                                                 int64_t st, int tid) {
   ScaleRegs s;
   const int64_t blk0 = st * KB;
   const int nblk = static_cast<int>(g.nb - blk0 < KB ? g.nb - blk0 : KB);
-  const int r = tid >> 1;
   const int h = tid & 1;  // blocks 2h, 2h+1
-  const int64_t gm = g.m0 + r < g.m ? g.m0 + r : g.m - 1;
   // two 8-byte loads: a row's (d, sum) pairs are only 8-byte aligned, and the
   // second block may lie past the last block of the row
-  const uint8_t* src = g.A.ds + 8 * (gm * g.nb + blk0 + 2 * h);
+  const uint8_t* src = sl.act + 8 * blk0;
   uint2 p0 = make_uint2(0, 0), p1 = make_uint2(0, 0);
   if (2 * h < nblk) p0 = *reinterpret_cast<const uint2*>(src);
   if (2 * h + 1 < nblk) p1 = *reinterpret_cast<const uint2*>(src + 8);
   s.act = make_uint4(p0.x, p0.y, p1.x, p1.y);
   s.wgt = make_uint4(0, 0, 0, 0);
   if (tid < BN) {
-    const int64_t gn = g.n0 + tid < g.n ? g.n0 + tid : g.n - 1;
     if constexpr (TYPE == kQ4_K) {
-      s.wgt = load16(g.W.row(gn) + 16 * (blk0 >> 3));
+      s.wgt = load16(sl.wgt + 16 * (blk0 >> 3));
     } else {
       // 16 bytes of scales; the padded header region keeps this in bounds
-      s.wgt = load16(g.W.row(gn) + 4 * blk0);
+      s.wgt = load16(sl.wgt + 4 * blk0);
     }
   }
   return s;
@@ -296,7 +340,9 @@ __device__ __forceinline__ void compute(const Stage<TYPE>* __restrict__ S, int n
 // declaring them restrict lets the compiler see that the compute's LDS reads
 // never wait for the direct loads into `nxt`.
 template <int TYPE>
-__device__ __forceinline__ bool step(const GemmCtx<TYPE>& g, const Stage<TYPE>* __restrict__ cur,
+__device__ __forceinline__ bool step(const GemmCtx<TYPE>& g, const DmaLanes<TYPE>& dl,
+                                     const ScaleLanes& sl,
+                                     const Stage<TYPE>* __restrict__ cur,
                                      Stage<TYPE>* __restrict__ nxt, int64_t st, int64_t steps,
                                      int tid, int wave, int lane, int wm0, int wn0, int half,
                                      int l32, const v16i& cinit, Acc& acc) {
@@ -307,8 +353,8 @@ __device__ __forceinline__ bool step(const GemmCtx<TYPE>& g, const Stage<TYPE>* 
   if (more) {
     // scale loads first: vmcnt retires in order, so waiting for them later
     // does not wait for the code loads issued after them
-    sc = load_scales<TYPE>(g, st + 1, tid);
-    issue_codes<TYPE>(g, nxt, st + 1, wave, lane);
+    sc = load_scales<TYPE>(g, sl, st + 1, tid);
+    issue_codes<TYPE>(g, dl, nxt, st + 1, wave);
   }
   const int nblk = static_cast<int>(g.nb - st * KB < KB ? g.nb - st * KB : KB);
   compute<TYPE>(cur, nblk, wm0, wn0, half, l32, cinit, acc);
@@ -356,13 +402,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n,
 
   const int64_t steps = (nb + KB - 1) / KB;
   // prologue: step 0 into s0
-  store_scales<TYPE>(&s0, load_scales<TYPE>(g, 0, tid), 0, tid);
-  issue_codes<TYPE>(g, &s0, 0, wave, lane);
+  const ScaleLanes sl = scale_lanes<TYPE>(g, tid);
+  store_scales<TYPE>(&s0, load_scales<TYPE>(g, sl, 0, tid), 0, tid);
+  const DmaLanes<TYPE> dl = dma_lanes<TYPE>(g, wave, lane);
+  issue_codes<TYPE>(g, dl, &s0, 0, wave);
 
   for (int64_t st = 0; st < steps; st += 2) {
-    if (!step<TYPE>(g, &s0, &s1, st, steps, tid, wave, lane, wm0, wn0, half, l32, cinit, acc))
+    if (!step<TYPE>(g, dl, sl, &s0, &s1, st, steps, tid, wave, lane, wm0, wn0, half, l32, cinit, acc))
       break;
-    if (!step<TYPE>(g, &s1, &s0, st + 1, steps, tid, wave, lane, wm0, wn0, half, l32, cinit,
+    if (!step<TYPE>(g, dl, sl, &s1, &s0, st + 1, steps, tid, wave, lane, wm0, wn0, half, l32, cinit,
                     acc))
       break;
   }
