@@ -15,6 +15,7 @@ thread_local int g_last_hip_error = 0;
 bool valid_type(int t) { return t == QBLK_Q4_0 || t == QBLK_Q8_0 || t == QBLK_Q4_K; }
 
 // Largest k accepted: row offsets inside the kernels are 32-bit.
+constexpr int64_t kMaxGemmK = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t{1} << 28;
 
 bool valid_k(int t, int64_t k) {
@@ -146,8 +147,11 @@ QBLK_EXPORT int qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const 
                           int64_t m, float* y, int64_t ldy, hipStream_t stream) {
   const int st = check_product(type, wq, n, k, xq, m, y, ldy);
   if (st != QBLK_OK || n == 0 || m == 0) return st;
-  // grid: x = n / 128 workgroups of 256 work-items, y = m / 128 (<= 65535)
-  if (256 * ((n + 127) / 128) > kMaxGridThreads || (m + 127) / 128 > 65535)
+  // grid: x = n / 128 workgroups of 256 work-items, y = m / 128 (<= 65535);
+  // a workgroup addresses its 128 activation / weight rows with 32-bit
+  // offsets, so k is limited to 2^24
+  if (256 * ((n + 127) / 128) > kMaxGridThreads || (m + 127) / 128 > 65535 ||
+      k > kMaxGemmK)
     return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_gemm(type, wq, n, k, xq, m, y, ldy, stream));

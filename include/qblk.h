@@ -191,7 +191,8 @@ int qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const float *x
 /*
  * Prefill-path product: the same result as qblk_gemv for m activation rows,
  * Y[m][ldy] = X * W^T, computed with int8 matrix-core tiles. Any m >= 0.
- * Errors as qblk_gemv (no batch limit).
+ * Errors as qblk_gemv (no batch limit), plus QBLK_ERR_UNSUPPORTED for
+ * k > 2^24.
  */
 int qblk_gemm(int type, const void *wq, int64_t n, int64_t k, const void *xq,
               int64_t m, float *y, int64_t ldy, hipStream_t stream);

@@ -104,6 +104,8 @@ def test_product_argument_validation():
     assert lib.qblk_gemv(3, _p(FAKE), 16, 256, _p(FAKE), 65, _p(FAKE), 16, NULL) == ERR_UNSUPPORTED
     assert lib.qblk_gemm(3, _p(FAKE), 16, 256, _p(FAKE), 65536 * 128, _p(FAKE), 16,
                          NULL) == ERR_UNSUPPORTED
+    assert lib.qblk_gemm(3, _p(FAKE), 16, (1 << 24) + 256, _p(FAKE), 4, _p(FAKE), 16,
+                         NULL) == ERR_UNSUPPORTED
 
 
 def test_quantize_and_pack_argument_validation():
