@@ -53,6 +53,12 @@ R7  Q4_K zero point: the sub-block minimum, but never above 0, so that one
 R8  Q4_K d and d_min are the smallest fp16 values that let the 6-bit codes
     cover every sub-block, and sc_j / mn_j are the smallest codes that cover
     sub-block j; this guarantees |x - x^| <= (d*sc_j)/2 (see quantize_q4_k).
+R9  The pages' own Q4_0 block ([P2] §5.3: one fp16 scale and 32 4-bit
+    integers, 144 bits) is a second 4-bit symmetric type, Q4_0_F16: the
+    scale is the fp32 amax/7 of R1/R2 rounded to the nearest fp16 (ties to
+    even; values beyond the fp16 range saturate at 65504), and the codes are
+    taken against that stored scale, q = round_half_away(x / d16) in fp32,
+    clamped to [-7, 7], so that x^ = q * d16 is what the decoder rebuilds.
 
 Packed byte layouts (the library's own, little-endian, described in
 include/qblk.h) are produced by the pack_* functions below.
@@ -67,6 +73,7 @@ SUBS = QK_K // QK  # 8 sub-blocks per super-block ([P4])
 TYPE_Q4_0 = 1
 TYPE_Q8_0 = 2
 TYPE_Q4_K = 3
+TYPE_Q4_0_F16 = 4
 
 # byte order of the 8 elements of a group of eight inside every int8 block of
 # the activation buffer and of Q8_0 weights: even elements first, then odd
@@ -176,6 +183,37 @@ def quantize_q4_0(w):
     return quantize_symmetric(w, 7)
 
 
+def fp16_round(x):
+    """Nearest IEEE binary16 value of each fp32 number (ties to even), as
+    float32; finite values beyond the fp16 range saturate at 65504 (R9)."""
+    x = np.asarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        h = x.astype(np.float16)
+    h = np.where(np.isfinite(h), h, np.copysign(np.float16(65504), x))
+    return h.astype(np.float32)
+
+
+def quantize_q4_0_f16(w):
+    """[P2] §5.3 Q4_0 as printed, with an fp16 scale (reading R9).
+
+    w: float32 [..., K]. Returns (q int64 [..., K], d16 float32 [..., K/32]
+    holding fp16 values): d16 = fp16(amax / 7), q = round_half_away(x / d16)
+    in fp32, clamped to [-7, 7]; d16 == 0 gives q == 0.
+    """
+    x = np.asarray(w, dtype=np.float32)
+    K = x.shape[-1]
+    if K % QK:
+        raise ValueError("K must be a multiple of 32")
+    xb = x.reshape(x.shape[:-1] + (K // QK, QK))
+    amax = np.max(np.abs(xb), axis=-1)
+    d16 = fp16_round((amax / np.float32(7)).astype(np.float32))
+    safe = np.where(d16 == 0, np.float32(1), d16).astype(np.float32)
+    v = (xb / safe[..., None]).astype(np.float32)      # fp32 IEEE division
+    q = np.clip(round_half_away(v.astype(np.float64)), -7, 7)
+    q = np.where((d16 == 0)[..., None], 0, q).astype(np.int64)
+    return q.reshape(x.shape), d16
+
+
 def dequant_symmetric(q, d):
     """x^ = Q * scale ([P2] §5.1), per 32-block, in fp64."""
     q = np.asarray(q, dtype=np.float64)
@@ -279,12 +317,16 @@ def row_bytes(wtype, K):
         return _pad16(4 * (K // QK)) + 32 * (K // QK)
     if wtype == TYPE_Q4_K:
         return 16 * (K // QK_K) + 128 * (K // QK_K)
+    if wtype == TYPE_Q4_0_F16:
+        return _pad16(2 * (K // QK)) + 16 * (K // QK)
     raise ValueError("unknown type")
 
 
 def header_bytes(wtype, K):
     if wtype in (TYPE_Q4_0, TYPE_Q8_0):
         return _pad16(4 * (K // QK))
+    if wtype == TYPE_Q4_0_F16:
+        return _pad16(2 * (K // QK))
     return 16 * (K // QK_K)
 
 
@@ -328,6 +370,20 @@ def pack_q4_0(q, d):
     out = np.zeros((N, row_bytes(TYPE_Q4_0, K)), dtype=np.uint8)
     out[:, :4 * nb] = np.asarray(d, dtype='<f4').reshape(N, nb).view(np.uint8)
     h = header_bytes(TYPE_Q4_0, K)
+    out[:, h:] = _nibble_pairs(q + 8).reshape(N, 16 * nb)
+    return out
+
+
+def pack_q4_0_f16(q, d16):
+    """Rows of [fp16 d per block | pad to 16 B][16 B of nibbles per block],
+    nibble = q + 8: [P2] §5.3's 18 bytes per 32 weights, split by row into a
+    scale region and a code region like the other types."""
+    q = np.asarray(q, dtype=np.int64)
+    N, K = q.shape
+    nb = K // QK
+    out = np.zeros((N, row_bytes(TYPE_Q4_0_F16, K)), dtype=np.uint8)
+    out[:, :2 * nb] = np.asarray(d16, dtype='<f2').reshape(N, nb).view(np.uint8)
+    h = header_bytes(TYPE_Q4_0_F16, K)
     out[:, h:] = _nibble_pairs(q + 8).reshape(N, 16 * nb)
     return out
 
@@ -404,6 +460,18 @@ def unpack_q4_0(packed, K):
     q[:, 0::2] = (nib & 15) - 8
     q[:, 1::2] = (nib >> 4) - 8
     return q, d
+
+
+def unpack_q4_0_f16(packed, K):
+    packed = np.asarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    nb = K // QK
+    d16 = packed[:, :2 * nb].copy().view('<f2').reshape(N, nb).astype(np.float32)
+    nib = packed[:, header_bytes(TYPE_Q4_0_F16, K):].astype(np.int64)
+    q = np.empty((N, K), dtype=np.int64)
+    q[:, 0::2] = (nib & 15) - 8
+    q[:, 1::2] = (nib >> 4) - 8
+    return q, d16
 
 
 def unpack_q8_0(packed, K):
@@ -514,13 +582,16 @@ def encode_weights(wtype, w):
     if wtype == TYPE_Q4_K:
         enc = quantize_q4_k(w)
         return pack_q4_k(enc), enc
+    if wtype == TYPE_Q4_0_F16:
+        q, d = quantize_q4_0_f16(w)
+        return pack_q4_0_f16(q, d), dict(q=q, d=d)
     raise ValueError("unknown type")
 
 
 def product(wtype, enc, act):
     """y32, y64 [M, N] for encoded weights and (q, d, s) activations."""
     aq, da, sa = act
-    if wtype in (TYPE_Q4_0, TYPE_Q8_0):
+    if wtype in (TYPE_Q4_0, TYPE_Q8_0, TYPE_Q4_0_F16):
         return product_sym(enc["q"], enc["d"], aq, da)
     return product_q4_k(enc, aq, da, sa)
 
@@ -533,7 +604,7 @@ def weight_codes_for_sums(wtype, enc):
 
 
 def dequant_weights(wtype, enc):
-    if wtype in (TYPE_Q4_0, TYPE_Q8_0):
+    if wtype in (TYPE_Q4_0, TYPE_Q8_0, TYPE_Q4_0_F16):
         return dequant_symmetric(enc["q"], enc["d"])
     return dequant_q4_k(enc)
 

@@ -5,7 +5,7 @@ import pytest
 
 from oracle import qblk_oracle as o
 
-TYPES = [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K]
+TYPES = [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K, o.TYPE_Q4_0_F16]
 
 
 def _blocks_with_special_cases(rng, rows, K, std=0.02):
@@ -180,7 +180,8 @@ def test_pack_unpack_round_trip(wtype):
         for k in enc:
             assert np.array_equal(back[k], enc[k]), k
     else:
-        unpack = o.unpack_q4_0 if wtype == o.TYPE_Q4_0 else o.unpack_q8_0
+        unpack = {o.TYPE_Q4_0: o.unpack_q4_0, o.TYPE_Q8_0: o.unpack_q8_0,
+                  o.TYPE_Q4_0_F16: o.unpack_q4_0_f16}[wtype]
         q, d = unpack(packed, 512)
         assert np.array_equal(q, enc["q"]) and np.array_equal(d, enc["d"])
 
@@ -223,7 +224,7 @@ def test_block_sums_small_k_symmetric(K):
     rng = np.random.default_rng(K)
     w = rng.standard_normal((3, K)).astype(np.float32)
     x = rng.standard_normal((2, K)).astype(np.float32)
-    for wtype in (o.TYPE_Q4_0, o.TYPE_Q8_0):
+    for wtype in (o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_0_F16):
         _, enc = o.encode_weights(wtype, w)
         aq, _, _ = o.quantize_act(x)
         assert o.block_sums(enc["q"], aq).tolist() == _brute_block_sums(
@@ -267,3 +268,18 @@ def test_power_of_two_scales_product_is_exact():
     y32, y64 = o.product_sym(q, d, aq, da)
     ref = (xi @ q.T) * 2.0 ** -9
     assert np.array_equal(y64, ref)
+
+
+def test_q4_0_f16_round_trip_bound_and_ranges():
+    """Codes in [-7, 7] against the stored fp16 scale, |x - q*d16| <= d16/2
+    (the fp32 quotient's rounding aside), blocks with outliers included."""
+    rng = np.random.default_rng(31)
+    w = _blocks_with_special_cases(rng, 16, 1024)
+    q, d = o.quantize_q4_0_f16(w)
+    assert q.min() >= -7 and q.max() <= 7
+    rec = o.dequant_symmetric(q, d)
+    err = np.abs(w.astype(np.float64) - rec).reshape(16, 32, 32)
+    bound = np.asarray(d, np.float64)[..., None] * (0.5 + 1e-6)
+    assert np.all(err <= bound)
+    # the stored scale is an fp16 value
+    assert np.array_equal(np.asarray(d).astype(np.float16).astype(np.float32), d)

@@ -130,3 +130,27 @@ def test_mutant_group8_order_is_caught(monkeypatch):
     monkeypatch.setattr(o, "GROUP8_ORDER", np.array([0, 1, 2, 3, 4, 5, 6, 7]))
     with pytest.raises(AssertionError):
         inv.test_activation_buffer_layout()
+
+
+def test_mutant_q4_0_f16_codes_against_fp32_scale_is_caught(monkeypatch):
+    """Codes taken against the unrounded fp32 scale instead of the stored
+    fp16 one: some element is then not at its nearest multiple of d16."""
+    def mutant(w):
+        q, d32 = o.quantize_symmetric(w, 7)
+        return q, o.fp16_round(d32)
+    monkeypatch.setattr(o, "quantize_q4_0_f16", mutant)
+    with pytest.raises(AssertionError):
+        inv.test_q4_0_f16_round_trip_bound_and_ranges()
+
+
+def test_mutant_q4_0_f16_truncated_scale_is_caught(monkeypatch):
+    """fp16 scale by truncation instead of rounding to nearest."""
+    def trunc16(x):
+        x = np.asarray(x, np.float32)
+        h = x.astype(np.float16)
+        over = np.abs(h.astype(np.float32)) > np.abs(x)
+        step = np.nextafter(h, np.float16(0))
+        return np.where(over, step, h).astype(np.float32)
+    monkeypatch.setattr(o, "fp16_round", trunc16)
+    with pytest.raises(AssertionError):
+        pins.test_q4_0_f16_scale_is_nearest_half_of_amax_over_7()

@@ -3,6 +3,7 @@ routines / brute force. CPU only."""
 
 import json
 import os
+import struct
 from decimal import Decimal, ROUND_HALF_UP
 
 import numpy as np
@@ -65,6 +66,49 @@ def test_bits_per_weight_closed_forms():
     assert o.row_bytes(o.TYPE_Q4_K, K) / K * 8 == 4.5
     # activation buffer: 8-bit codes + fp32 scale + int32 sum per 32
     assert o.act_bytes(3, K) * 8 == 3 * K * (8 + 64 / 32)
+    # the page's own Q4_0 block (fp16 scale): exactly its 144 bits, 4.5 bpw
+    assert o.row_bytes(o.TYPE_Q4_0_F16, K) * 8 == g["q4_0"]["total_bits"] * K // 32
+    assert o.row_bytes(o.TYPE_Q4_0_F16, K) * 8 / K == g["q4_0"]["bpw"]
+
+
+def test_q4_0_f16_example_symmetric_rule():
+    """runguoli page §5.1 example under the page's fp16-scale Q4_0 (§5.3):
+    scale 0.5 is an fp16 value, so the codes and reconstruction are the
+    printed ones."""
+    g = _golden("p2_q4_0_example.json")
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :5] = g["weights"]
+    q, d = o.quantize_q4_0_f16(x)
+    assert float(d[0, 0]) == g["scale"]
+    assert q[0, :5].tolist() == g["codes"]
+    assert o.dequant_symmetric(q, d)[0, :5].tolist() == g["reconstructed"]
+
+
+def _struct_half(v):
+    """Nearest binary16 of a float by the standard library's IEEE half
+    conversion (ties to even); OverflowError beyond the fp16 range."""
+    return struct.unpack("<e", struct.pack("<e", float(v)))[0]
+
+
+def test_q4_0_f16_scale_is_nearest_half_of_amax_over_7():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((64, 32 * 16)) * 10.0 ** rng.uniform(-6, 3, (64, 1))).astype(np.float32)
+    q, d = o.quantize_q4_0_f16(w)
+    amax = np.max(np.abs(w.reshape(64, 16, 32)), axis=-1)
+    for r in range(64):
+        for b in range(16):
+            d32 = np.float32(amax[r, b]) / np.float32(7)
+            try:
+                ref = _struct_half(d32)
+            except OverflowError:
+                ref = 65504.0
+            assert float(d[r, b]) == ref
+    # saturation and an all-zero block
+    big = np.zeros((1, 64), dtype=np.float32)
+    big[0, 0] = 1e6
+    qb, db = o.quantize_q4_0_f16(big)
+    assert float(db[0, 0]) == 65504.0 and qb[0, 0] == 7
+    assert float(db[0, 1]) == 0.0 and np.all(qb[0, 32:] == 0)
 
 
 # ---------------------------------------------------------------- scalar kernel of §6.4
@@ -100,6 +144,30 @@ def test_q4_0_pack_matches_page_scalar_kernel():
         ref = float(deq[n] @ yf)
         got = _page_q4_0_float_dot(packed[n], K, yf)
         assert abs(got - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_q4_0_f16_pack_matches_page_scalar_kernel():
+    """The same scalar kernel reading fp16 scales: the page's 18-byte block."""
+    rng = np.random.default_rng(12)
+    K = 256
+    nb = K // 32
+    w = (rng.standard_normal((3, K)) * 0.02).astype(np.float32)
+    yf = rng.standard_normal(K)
+    packed, enc = o.encode_weights(o.TYPE_Q4_0_F16, w)
+    deq = o.dequant_weights(o.TYPE_Q4_0_F16, enc)
+    for n in range(3):
+        row = packed[n]
+        scales = row[:2 * nb].copy().view("<f2")
+        qs = row[o.header_bytes(o.TYPE_Q4_0_F16, K):]
+        total = 0.0
+        for blk in range(nb):
+            scale = float(scales[blk])
+            for j in range(16):
+                byte = int(qs[16 * blk + j])
+                total += (((byte & 0x0F) - 8) * scale) * float(yf[32 * blk + 2 * j])
+                total += (((byte >> 4) - 8) * scale) * float(yf[32 * blk + 2 * j + 1])
+        ref = float(deq[n] @ yf)
+        assert abs(total - ref) <= 1e-12 * max(1.0, abs(ref))
 
 
 def test_q4_0_pack_nibble_order_is_pinned():
