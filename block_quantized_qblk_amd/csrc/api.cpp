@@ -12,7 +12,9 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-bool valid_type(int t) { return t == QBLK_Q4_0 || t == QBLK_Q8_0 || t == QBLK_Q4_K; }
+bool valid_type(int t) {
+  return t == QBLK_Q4_0 || t == QBLK_Q8_0 || t == QBLK_Q4_K || t == QBLK_Q4_0_F16;
+}
 
 // Largest k accepted: row offsets inside the kernels are 32-bit.
 constexpr int64_t kMaxGemmK = int64_t(1) << 24;

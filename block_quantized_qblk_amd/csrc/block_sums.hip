@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void block_sums_kernel(WeightView W, int64_t n
     S = dot_i8x32(load16(wquant + 32 * blk), load16(wquant + 32 * blk + 16), a0, a1, 0);
   } else {
     S = dot_nib32(load16(wquant + 16 * blk), a0, a1, 0);
-    if constexpr (TYPE == kQ4_0) S -= 8 * __float_as_int(A.dsum(mm, blk).y);
+    if constexpr (TYPE == kQ4_0 || TYPE == kQ4_0H) S -= 8 * __float_as_int(A.dsum(mm, blk).y);
   }
   out[gid] = S;
 }
@@ -46,6 +46,7 @@ hipError_t launch_block_sums(int type, const void* wq, int64_t n, int64_t k, con
   switch (type) {
     case kQ4_0: hipLaunchKernelGGL(block_sums_kernel<kQ4_0>, g, dim3(256), 0, s, W, n, nb, A, m, sums); break;
     case kQ8_0: hipLaunchKernelGGL(block_sums_kernel<kQ8_0>, g, dim3(256), 0, s, W, n, nb, A, m, sums); break;
+    case kQ4_0H: hipLaunchKernelGGL(block_sums_kernel<kQ4_0H>, g, dim3(256), 0, s, W, n, nb, A, m, sums); break;
     default: hipLaunchKernelGGL(block_sums_kernel<kQ4_K>, g, dim3(256), 0, s, W, n, nb, A, m, sums); break;
   }
   return hipGetLastError();

@@ -208,6 +208,10 @@ __device__ __forceinline__ ScaleRegs load_scales(const GemmCtx<TYPE>& g, const S
   if (tid < BN) {
     if constexpr (TYPE == kQ4_K) {
       s.wgt = load16(sl.wgt + 16 * (blk0 >> 3));
+    } else if constexpr (TYPE == kQ4_0H) {
+      // 8 bytes of fp16 scales; the padded header region keeps this in bounds
+      const uint2 h = *reinterpret_cast<const uint2*>(sl.wgt + 2 * blk0);
+      s.wgt = make_uint4(h.x, h.y, 0, 0);
     } else {
       // 16 bytes of scales; the padded header region keeps this in bounds
       s.wgt = load16(sl.wgt + 4 * blk0);
@@ -239,8 +243,14 @@ __device__ __forceinline__ void store_scales(Stage<TYPE>* __restrict__ S, const 
         S->mn.wm[jj][tid] = dmin * static_cast<float>(q4k_mn(s.wgt, j0 + jj));
       }
     } else {
-      const float dw[4] = {__uint_as_float(s.wgt.x), __uint_as_float(s.wgt.y),
-                           __uint_as_float(s.wgt.z), __uint_as_float(s.wgt.w)};
+      float dw[4] = {__uint_as_float(s.wgt.x), __uint_as_float(s.wgt.y),
+                     __uint_as_float(s.wgt.z), __uint_as_float(s.wgt.w)};
+      if constexpr (TYPE == kQ4_0H) {
+        dw[0] = half_bits_to_float(s.wgt.x);
+        dw[1] = half_bits_to_float(s.wgt.x >> 16);
+        dw[2] = half_bits_to_float(s.wgt.y);
+        dw[3] = half_bits_to_float(s.wgt.y >> 16);
+      }
 #pragma unroll
       for (int jj = 0; jj < KB; ++jj) {
         S->sw[jj][tid] = dw[jj];
@@ -444,6 +454,7 @@ hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const voi
   switch (type) {
     case kQ4_0: hipLaunchKernelGGL(gemm_kernel<kQ4_0>, grid, dim3(kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
     case kQ8_0: hipLaunchKernelGGL(gemm_kernel<kQ8_0>, grid, dim3(kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
+    case kQ4_0H: hipLaunchKernelGGL(gemm_kernel<kQ4_0H>, grid, dim3(kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
     default: hipLaunchKernelGGL(gemm_kernel<kQ4_K>, grid, dim3(kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
   }
   return hipGetLastError();

@@ -31,6 +31,8 @@ template <>
 struct WChunk<kQ4_K> { uint4 q; };
 template <>
 struct WChunk<kQ8_0> { uint4 q0, q1; };
+template <>
+struct WChunk<kQ4_0H> { uint4 q; };
 
 template <int TYPE>
 struct WScale;  // one lane's block scale data
@@ -40,6 +42,8 @@ template <>
 struct WScale<kQ8_0> { float d; };
 template <>
 struct WScale<kQ4_K> { uint4 h; };
+template <>
+struct WScale<kQ4_0H> { float d; };
 
 // Loads of one lane's block `blk` of a row whose (wave-uniform) base is in
 // scalar registers: 32-bit lane offsets let the loads use a scalar base.
@@ -51,6 +55,9 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ wrow, uin
     w.q = load_stream16(wrow + (hdr_bytes + 16u * blk));
   } else if constexpr (TYPE == kQ4_0) {
     s.d = __uint_as_float(load_stream4(wrow + 4u * blk));
+    w.q = load_stream16(wrow + (hdr_bytes + 16u * blk));
+  } else if constexpr (TYPE == kQ4_0H) {
+    s.d = half_bits_to_float(load_stream2(wrow + 2u * blk));
     w.q = load_stream16(wrow + (hdr_bytes + 16u * blk));
   } else {
     s.d = __uint_as_float(load_stream4(wrow + 4u * blk));
@@ -186,7 +193,7 @@ __device__ __forceinline__ void block_fma(uint32_t lane, const WChunk<TYPE>& w,
       const float asum = static_cast<float>(__float_as_int(ds[b][u].y));
       acc[b] = fmaf(ds[b][u].x, fmaf(sw, static_cast<float>(S), wm * asum), acc[b]);
     }
-  } else if constexpr (TYPE == kQ4_0) {
+  } else if constexpr (TYPE == kQ4_0 || TYPE == kQ4_0H) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const int S = dot_nib32(w.q, a[b][u][0], a[b][u][1], 0) - 8 * __float_as_int(ds[b][u].y);
@@ -616,6 +623,7 @@ hipError_t launch_type(int type, int b, const Plan& p, hipStream_t s) {
   switch (type) {
     case kQ4_0: return launch_batch<kQ4_0, MODE>(b, p, s);
     case kQ8_0: return launch_batch<kQ8_0, MODE>(b, p, s);
+    case kQ4_0H: return launch_batch<kQ4_0H, MODE>(b, p, s);
     default: return launch_batch<kQ4_K, MODE>(b, p, s);
   }
 }

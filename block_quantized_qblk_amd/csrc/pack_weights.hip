@@ -2,7 +2,9 @@
 //
 // Q4_0 / Q8_0: "llama.cpp 推理引擎" §5.1 (symmetric rule) with b = 4 (codes in
 // [-7, 7], stored as nibble q + 8, §5.3 and the §6.4 nibble order) or b = 8
-// (§5.4), fp32 scale, decisions in fp32 with IEEE division.
+// (§5.4), fp32 scale, decisions in fp32 with IEEE division. Q4_0_F16 (§5.3's
+// own block): the same with the scale rounded to the nearest fp16 (ties to
+// even, saturating at 65504) before the codes are taken against it.
 //
 // Q4_K: §5.2 (asymmetric rule, zero point = block minimum) inside the §5.5
 // hierarchy: 256-element super-blocks of 8 sub-blocks of 32 (also "llama.cpp：
@@ -32,8 +34,8 @@ __device__ __forceinline__ uint2 pack_group8(const int (&q)[8]) {
   return r;
 }
 
-// Q4_0 (QMAX 7) and Q8_0 (QMAX 127): four lanes per 32-block.
-template <int QMAX>
+// Q4_0 (QMAX 7) and Q8_0 (QMAX 127), F16: Q4_0_F16; four lanes per 32-block.
+template <int QMAX, bool F16 = false>
 __global__ __launch_bounds__(256) void pack_sym_kernel(const float* __restrict__ w, int64_t n,
                                                        int64_t k, int64_t ldw,
                                                        uint8_t* __restrict__ wq, int64_t rb,
@@ -56,7 +58,13 @@ __global__ __launch_bounds__(256) void pack_sym_kernel(const float* __restrict__
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(e[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  const float d = __fdiv_rn(amax, static_cast<float>(QMAX));
+  float d = __fdiv_rn(amax, static_cast<float>(QMAX));
+  _Float16 d16 = 0;
+  if constexpr (F16) {
+    d16 = static_cast<_Float16>(fminf(d, 65504.0f));  // round to nearest even
+    if (d > 65504.0f) d16 = static_cast<_Float16>(65504.0f);
+    d = static_cast<float>(d16);
+  }
 
   int q[8];
 #pragma unroll
@@ -71,10 +79,19 @@ __global__ __launch_bounds__(256) void pack_sym_kernel(const float* __restrict__
   }
 
   uint8_t* dst = wq + row * rb;
-  if (sub == 0) *reinterpret_cast<float*>(dst + 4 * blk) = d;
-  // zero the padding at the end of the header region
-  if (blk == nb - 1 && sub > 0 && 4 * (nb + sub - 1) < hb)
-    *reinterpret_cast<uint32_t*>(dst + 4 * (nb + sub - 1)) = 0u;
+  if constexpr (F16) {
+    if (sub == 0) *reinterpret_cast<_Float16*>(dst + 2 * blk) = d16;
+    // zero the padding at the end of the header region (up to 7 halves)
+    if (blk == nb - 1) {
+      if (2 * (nb + sub) < hb) *reinterpret_cast<uint16_t*>(dst + 2 * (nb + sub)) = 0;
+      if (2 * (nb + sub + 4) < hb) *reinterpret_cast<uint16_t*>(dst + 2 * (nb + sub + 4)) = 0;
+    }
+  } else {
+    if (sub == 0) *reinterpret_cast<float*>(dst + 4 * blk) = d;
+    // zero the padding at the end of the header region
+    if (blk == nb - 1 && sub > 0 && 4 * (nb + sub - 1) < hb)
+      *reinterpret_cast<uint32_t*>(dst + 4 * (nb + sub - 1)) = 0u;
+  }
 
   if constexpr (QMAX == 7) {
     uint32_t packed = 0;
@@ -240,6 +257,9 @@ hipError_t launch_pack_weights(int type, const float* w, int64_t n, int64_t k, i
     if (type == kQ4_0) {
       hipLaunchKernelGGL(pack_sym_kernel<7>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s,
                          w, n, k, ldw, out, rb, hb);
+    } else if (type == kQ4_0H) {
+      hipLaunchKernelGGL((pack_sym_kernel<7, true>), dim3(static_cast<uint32_t>(grid)), dim3(256),
+                         0, s, w, n, k, ldw, out, rb, hb);
     } else {
       hipLaunchKernelGGL(pack_sym_kernel<127>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
                          s, w, n, k, ldw, out, rb, hb);

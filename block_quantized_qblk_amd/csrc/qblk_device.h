@@ -22,6 +22,9 @@ __device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
 __device__ __forceinline__ uint32_t load_stream4(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
+__device__ __forceinline__ uint32_t load_stream2(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

@@ -8,7 +8,7 @@
 
 namespace qblk {
 
-enum : int { kQ4_0 = 1, kQ8_0 = 2, kQ4_K = 3 };
+enum : int { kQ4_0 = 1, kQ8_0 = 2, kQ4_K = 3, kQ4_0H = 4 };  // kQ4_0H: fp16-scale Q4_0
 
 inline int64_t pad16(int64_t v) { return (v + 15) / 16 * 16; }
 
@@ -18,6 +18,7 @@ inline int64_t header_bytes(int type, int64_t k) {
     case kQ4_0:
     case kQ8_0: return pad16(4 * (k / 32));
     case kQ4_K: return 16 * (k / 256);
+    case kQ4_0H: return pad16(2 * (k / 32));
     default: return 0;
   }
 }
@@ -28,6 +29,7 @@ inline int64_t row_bytes(int type, int64_t k) {
     case kQ4_0: return header_bytes(type, k) + 16 * (k / 32);
     case kQ8_0: return header_bytes(type, k) + 32 * (k / 32);
     case kQ4_K: return header_bytes(type, k) + 128 * (k / 256);
+    case kQ4_0H: return header_bytes(type, k) + 16 * (k / 32);
     default: return 0;
   }
 }

@@ -11,8 +11,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqblk.so")
 
-Q4_0, Q8_0, Q4_K = 1, 2, 3
-TYPES = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K}
+Q4_0, Q8_0, Q4_K, Q4_0_F16 = 1, 2, 3, 4
+TYPES = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q4_0_F16": Q4_0_F16}
 GEMV_MAX_BATCH = 64
 
 _lib = None

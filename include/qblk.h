@@ -34,6 +34,8 @@
  *              [16 B x nb: byte t of block b = (q[32b+2t]+8) | (q[32b+2t+1]+8) << 4]
  *              codes q in [-7, 7] when packed by this library; any nibble
  *              0..15 decodes as nibble - 8.
+ *   Q4_0_F16 row: [fp16 d x nb, zero-padded to a multiple of 16 B]
+ *              [16 B x nb: the Q4_0 nibbles]
  *   Q8_0 row : [fp32 d x nb, zero-padded to a multiple of 16 B]
  *              [32 int8 x nb; inside a block each group of 8 codes is stored
  *               in the element order 0,2,4,6,1,3,5,7]
@@ -69,7 +71,10 @@ extern "C" {
 typedef enum {
   QBLK_Q4_0 = 1, /* 32-blocks, 4-bit codes, fp32 scale: 20 B / 32 weights */
   QBLK_Q8_0 = 2, /* 32-blocks, int8 codes, fp32 scale: 36 B / 32 weights  */
-  QBLK_Q4_K = 3  /* 256-element super-blocks, 144 B / 256 weights         */
+  QBLK_Q4_K = 3, /* 256-element super-blocks, 144 B / 256 weights         */
+  QBLK_Q4_0_F16 = 4 /* 32-blocks, 4-bit codes, fp16 scale: 18 B / 32 weights,
+                       the pages' own Q4_0 block ("llama.cpp 推理引擎",
+                       §5.3) */
 } qblk_type;
 
 typedef enum {
@@ -114,7 +119,9 @@ size_t qblk_act_bytes(int64_t m, int64_t k);
  *   w   : fp32 [n][ldw], row n holds the k weights of output channel n.
  *   wq  : out, qblk_weight_bytes(type, n, k) bytes, layout above.
  * Rounding is half away from zero. Q4_0/Q8_0 decisions are taken in fp32
- * with IEEE division; Q4_K decisions in fp64:
+ * with IEEE division. Q4_0_F16: d = fp16 nearest (ties to even) of the fp32
+ * amax/7, saturating at 65504, and q = round(x / d) against that fp16 d.
+ * Q4_K decisions in fp64:
  *   m_j  = max(0, -min of sub-block j); d_min = -(smallest fp16 h with
  *   63*h >= max_j m_j); mn_j = smallest code with mn_j*h >= m_j;
  *   t_j  = max of sub-block j + mn_j*h; d = smallest fp16 with

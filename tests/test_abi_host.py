@@ -53,7 +53,7 @@ def test_exports_match_header():
 
 @pytest.mark.parametrize("k", [32, 96, 256, 416, 1024, 4096, 14336, 28672])
 def test_size_functions_match_oracle(k):
-    for t in (o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K):
+    for t in (o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K, o.TYPE_Q4_0_F16):
         if t == o.TYPE_Q4_K and k % 256:
             assert qblk.qblk_weight_row_bytes(t, k) == 0
             continue

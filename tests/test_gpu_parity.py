@@ -12,8 +12,8 @@ from tests.gpu_util import (REL_TOL, check_rel, dev, dev_pack, dev_quantize, exp
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K]
-TNAME = {1: "Q4_0", 2: "Q8_0", 3: "Q4_K"}
+TYPES = [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K, o.TYPE_Q4_0_F16]
+TNAME = {1: "Q4_0", 2: "Q8_0", 3: "Q4_K", 4: "Q4_0_F16"}
 
 
 def _special_rows(rng, n, k, std=0.02):
@@ -85,9 +85,10 @@ def test_pack_weights_bit_exact(wtype, n, k):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("wtype", [o.TYPE_Q4_0, o.TYPE_Q8_0])
+@pytest.mark.parametrize("wtype", [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_0_F16])
 def test_pack_weights_padded_header(wtype):
-    """k = 416: 13 blocks, 52 header bytes padded to 64."""
+    """k = 416: 13 blocks, 52 header bytes padded to 64 (fp16 scales: 26
+    padded to 32)."""
     print(f"pack padded {TNAME[wtype]}", flush=True)
     rng = np.random.default_rng(3)
     w = _special_rows(rng, 9, 416)
@@ -96,6 +97,22 @@ def test_pack_weights_padded_header(wtype):
     qblk.qblk_pack_weights(wtype, dev(w), out=buf)
     ref, _ = o.encode_weights(wtype, w)
     assert np.array_equal(host(buf).reshape(9, -1), ref)
+
+
+def test_pack_q4_0_f16_extreme_scales():
+    """fp16 scales in the subnormal range, rounding to zero, and saturating
+    at 65504, next to ordinary rows."""
+    print("pack Q4_0_F16 extremes", flush=True)
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    w[0] *= 1e-4                      # d in the fp16 subnormal range
+    w[1] *= 1e-8                      # d rounds to zero: all codes 0
+    w[2] *= 1e8                       # d saturates at 65504
+    w[3, :32] = 0.0                   # zero block
+    w[4, 5] = 7.0 * 0.25              # amax/7 exactly an fp16 value
+    got = host(dev_pack(o.TYPE_Q4_0_F16, w)).reshape(6, -1)
+    ref, _ = o.encode_weights(o.TYPE_Q4_0_F16, w)
+    assert np.array_equal(got, ref)
 
 
 def test_pack_q4_k_extreme_ranges():
@@ -148,6 +165,9 @@ def _exact_case(wtype, n, k, m, seed):
     elif wtype == o.TYPE_Q4_0:
         enc = dict(q=rng.integers(-8, 8, (n, k)), d=np.full((n, nb), 2.0 ** -6, np.float32))
         packed = o.pack_q4_0(enc["q"], enc["d"])
+    elif wtype == o.TYPE_Q4_0_F16:
+        enc = dict(q=rng.integers(-8, 8, (n, k)), d=np.full((n, nb), 2.0 ** -6, np.float32))
+        packed = o.pack_q4_0_f16(enc["q"], enc["d"])
     else:
         enc = dict(q=rng.integers(-12, 13, (n, k)), d=np.full((n, nb), 2.0 ** -7, np.float32))
         packed = o.pack_q8_0(enc["q"], enc["d"])
