@@ -24,6 +24,7 @@ SOURCES = [
     "pack_weights.hip",
     "gemv.hip",
     "gemm.hip",
+    "gemm_small.hip",
     "block_sums.hip",
     "api.cpp",
 ]
@@ -43,7 +44,8 @@ COMMON = [
 # per-source extra flags: the GEMM's MFMA results feed VALU instructions
 # directly, so MFMAs write VGPRs instead of accumulation registers (no copy
 # back per result)
-EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gemm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

@@ -65,6 +65,10 @@ hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const
                            hipStream_t s);
 hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t m, float* y, int64_t ldy, hipStream_t s);
+// rows at or below which launch_gemm takes the few-rows form
+constexpr int64_t kGemmSmallMaxRows = 64;
+hipError_t launch_gemm_small(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+                             int64_t m, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                              int64_t m, int32_t* sums, hipStream_t s);
 

@@ -192,7 +192,7 @@ def test_gemv_exact_arithmetic(wtype, batch):
 
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("m", [1, 37, 130])
+@pytest.mark.parametrize("m", [1, 16, 37, 64, 130])
 def test_gemm_exact_arithmetic(wtype, m):
     print(f"gemm exact {TNAME[wtype]} m={m}", flush=True)
     n, k = 150, 1024 if wtype == o.TYPE_Q4_K else 1056
@@ -217,7 +217,8 @@ def test_gemv_random(wtype, n, k, batch):
 
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("m,n,k", [(1, 37, 256), (5, 300, 1024), (70, 129, 2304),
-                                   (130, 257, 512), (256, 128, 4096)])
+                                   (130, 257, 512), (256, 128, 4096), (16, 513, 2304),
+                                   (33, 100, 256), (64, 1000, 4096), (17, 47, 7168)])
 def test_gemm_random(wtype, m, n, k):
     print(f"gemm {TNAME[wtype]} m={m} n={n} k={k}", flush=True)
     rng = np.random.default_rng(41 * wtype + m + n)
