@@ -486,7 +486,9 @@ def gemm_bench(torch, qblk, synth, dev, iters, copies=16):
 
 def sym_bench(torch, qblk, synth, dev):
     """Q4_0 4096 x 4096 and Q8_0 14336 x 4096 GEMVs, batch 1, rotated over
-    enough copies to exceed the last-level cache."""
+    enough copies to exceed the last-level cache; beside each, the same
+    weights against the fp32 activation (qblk_gemv_float, no activation
+    quantization)."""
     res = {}
     for name, t, n, k in (("q4_0_gemv_4096x4096", qblk.Q4_0, 4096, 4096),
                           ("q8_0_gemv_14336x4096", qblk.Q8_0, 14336, 4096)):
@@ -497,12 +499,18 @@ def sym_bench(torch, qblk, synth, dev):
             w = synth.torch_weights("normal", 1000 * t + c, n, k, device=dev)
             wqs.append(qblk.qblk_pack_weights(t, w))
             del w
-        xq = qblk.qblk_quantize_act(synth.torch_activations(1000 * t + 99, 1, k, device=dev))
+        x = synth.torch_activations(1000 * t + 99, 1, k, device=dev)
+        xq = qblk.qblk_quantize_act(x)
         y = torch.empty((1, n), dtype=torch.float32, device=dev)
         us = timed_launches(torch, lambda i: qblk.qblk_gemv(t, wqs[i % copies], n, k, xq, 1, y=y),
                             100)
         res[name] = {"us": round(us, 3), "weight_bytes": wb, "GBps": round(wb / (us * 1e-6) / 1e9, 1)}
         log(f"{name}: {res[name]}")
+        fname = name.replace("_gemv_", "_gemv_float_")
+        us = timed_launches(torch, lambda i: qblk.qblk_gemv_float(t, wqs[i % copies], n, k, x, y=y),
+                            100)
+        res[fname] = {"us": round(us, 3), "weight_bytes": wb, "GBps": round(wb / (us * 1e-6) / 1e9, 1)}
+        log(f"{fname}: {res[fname]}")
         del wqs
         torch.cuda.empty_cache()
     return res

@@ -145,15 +145,28 @@ QBLK_EXPORT int qblk_gemv_f32(int type, const void* wq, int64_t n, int64_t k, co
   return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, work, stream));
 }
 
+QBLK_EXPORT int qblk_gemv_float(int type, const void* wq, int64_t n, int64_t k, const float* x,
+                                int64_t ldx, int64_t batch, float* y, int64_t ldy,
+                                hipStream_t stream) {
+  const int st = check_product(type, wq, n, k, x, batch, y, ldy);
+  if (st != QBLK_OK || n == 0 || batch == 0) return st;
+  if (ldx < k) return QBLK_ERR_SHAPE;
+  if (ldx % 4 != 0) return QBLK_ERR_ALIGN;
+  if (batch > QBLK_GEMV_MAX_BATCH) return QBLK_ERR_UNSUPPORTED;
+  if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(qblk::launch_gemv_float(type, wq, n, k, x, ldx, batch, y, ldy, stream));
+}
+
 QBLK_EXPORT int qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                           int64_t m, float* y, int64_t ldy, hipStream_t stream) {
   const int st = check_product(type, wq, n, k, xq, m, y, ldy);
   if (st != QBLK_OK || n == 0 || m == 0) return st;
-  // grid: x = n / 128 workgroups of 256 work-items, y = m / 128 (<= 65535);
-  // a workgroup addresses its 128 activation / weight rows with 32-bit
-  // offsets, so k is limited to 2^24
-  if (256 * ((n + 127) / 128) > kMaxGridThreads || (m + 127) / 128 > 65535 ||
-      k > kMaxGemmK)
+  // grid: x = n / 128 workgroups of 256 work-items, y = m / 128 (<= 65535),
+  // or, for m <= 64, x = n / 32; a workgroup addresses its activation and
+  // weight rows with 32-bit offsets, so k is limited to 2^24
+  const int64_t wgs = m <= qblk::kGemmSmallMaxRows ? (n + 31) / 32 : (n + 127) / 128;
+  if (256 * wgs > kMaxGridThreads || (m + 127) / 128 > 65535 || k > kMaxGemmK)
     return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_gemm(type, wq, n, k, xq, m, y, ldy, stream));

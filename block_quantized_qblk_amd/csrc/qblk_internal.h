@@ -63,6 +63,8 @@ inline int64_t gemv_f32_work_bytes(int64_t batch, int64_t k) {
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
                            int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
                            hipStream_t s);
+hipError_t launch_gemv_float(int type, const void* wq, int64_t n, int64_t k, const float* x,
+                             int64_t ldx, int64_t batch, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t m, float* y, int64_t ldy, hipStream_t s);
 // rows at or below which launch_gemm takes the few-rows form

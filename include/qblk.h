@@ -196,6 +196,25 @@ int qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const float *x
                   hipStream_t stream);
 
 /*
+ * Decode-path product with fp32 activations and no activation quantization,
+ * the form of the pages' scalar Q4_0 dot ("llama.cpp 推理引擎", §6.4: each
+ * weight decoded in place and multiplied by a float activation; Q4_K
+ * weights decoded as in §5.5): for b < batch, n < n,
+ *   y[b*ldy + n] = sum_k w[n][k] * x[b*ldx + k]
+ *   where w is the decoded weight: Q4_0 / Q4_0_F16 d*(nibble - 8), Q8_0 d*q,
+ *   Q4_K (d*sc_j)*q + (d_min*mn_j)*1. Accumulation is fp32 in an unspecified
+ *   (but fixed) order.
+ *   wq : packed weights [n] rows of k;  x : fp32 [batch][ldx], 16-byte
+ *   aligned, ldx a multiple of 4;  y : fp32 [batch][ldy].
+ * 1 <= batch <= QBLK_GEMV_MAX_BATCH.
+ * Errors: as qblk_gemv, plus QBLK_ERR_SHAPE for ldx < k and QBLK_ERR_ALIGN
+ * for x or ldx.
+ */
+int qblk_gemv_float(int type, const void *wq, int64_t n, int64_t k, const float *x,
+                    int64_t ldx, int64_t batch, float *y, int64_t ldy,
+                    hipStream_t stream);
+
+/*
  * Prefill-path product: the same result as qblk_gemv for m activation rows,
  * Y[m][ldy] = X * W^T, computed with int8 matrix-core tiles. Any m >= 0.
  * Errors as qblk_gemv (no batch limit), plus QBLK_ERR_UNSUPPORTED for

@@ -32,7 +32,8 @@ Sources (web pages; cited by title and section):
   sharing one scale (worked example with scale 0.08) and the K-quant
   hierarchy of 256-weight super-blocks made of 8 sub-blocks of 32.
 
-Readings where the pages are silent or disagree:
+Readings where the pages are silent or disagree (numbered as in the design
+notes; the ones without an effect on this module are not repeated here):
 
 R1  Q4_0 and Q8_0 scales are fp32 (the Q4_0 page text says fp16; the workload
     being reproduced states fp32 for both).
@@ -53,7 +54,11 @@ R7  Q4_K zero point: the sub-block minimum, but never above 0, so that one
 R8  Q4_K d and d_min are the smallest fp16 values that let the 6-bit codes
     cover every sub-block, and sc_j / mn_j are the smallest codes that cover
     sub-block j; this guarantees |x - x^| <= (d*sc_j)/2 (see quantize_q4_k).
-R9  The pages' own Q4_0 block ([P2] §5.3: one fp16 scale and 32 4-bit
+R12 [P2] §6.4's scalar kernel multiplies decoded weights by float
+    activations, while the Q4_K x Q8 dot of [P3] §2.2 quantizes them: the
+    hot path quantizes activations to Q8 32-blocks (R3); the float form is a
+    separate product (product_float) over the same packed weights.
+R18 The pages' own Q4_0 block ([P2] §5.3: one fp16 scale and 32 4-bit
     integers, 144 bits) is a second 4-bit symmetric type, Q4_0_F16: the
     scale is the fp32 amax/7 of R1/R2 rounded to the nearest fp16 (ties to
     even; values beyond the fp16 range saturate at 65504), and the codes are
@@ -185,7 +190,7 @@ def quantize_q4_0(w):
 
 def fp16_round(x):
     """Nearest IEEE binary16 value of each fp32 number (ties to even), as
-    float32; finite values beyond the fp16 range saturate at 65504 (R9)."""
+    float32; finite values beyond the fp16 range saturate at 65504 (R18)."""
     x = np.asarray(x, dtype=np.float32)
     with np.errstate(over="ignore"):
         h = x.astype(np.float16)
@@ -194,7 +199,7 @@ def fp16_round(x):
 
 
 def quantize_q4_0_f16(w):
-    """[P2] §5.3 Q4_0 as printed, with an fp16 scale (reading R9).
+    """[P2] §5.3 Q4_0 as printed, with an fp16 scale (reading R18).
 
     w: float32 [..., K]. Returns (q int64 [..., K], d16 float32 [..., K/32]
     holding fp16 values): d16 = fp16(amax / 7), q = round_half_away(x / d16)
@@ -564,6 +569,17 @@ def product_q4_k(enc, aq, da, sa):
 def dequant_dot(wdeq, adeq):
     """fp64 dot product of the dequantized operands: Y = adeq @ wdeq^T."""
     return np.asarray(adeq, np.float64) @ np.asarray(wdeq, np.float64).T
+
+
+def product_float(wtype, enc, x):
+    """Float-activation product (R12): [P2] §6.4's scalar Q4_0 kernel decodes
+    each weight in place, (nibble - 8) * d, and multiplies it by a float
+    activation; the other formats decode as their dequantization rule
+    ([P2] §5.4 Q8_0, §5.5 Q4_K). y[m, n] = sum_k w^[n, k] * x[m, k] with w^
+    the dequantized weights, in fp64 from the given x, rounded once.
+    Returns (y32, y64), shape [M, N]."""
+    y = dequant_dot(dequant_weights(wtype, enc), np.asarray(x, np.float64))
+    return y.astype(np.float32), y
 
 
 # --------------------------------------------------------------------------

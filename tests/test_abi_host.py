@@ -154,3 +154,19 @@ def test_gemv_f32_workspace_size_and_validation():
     assert f(3, w, 16, 256, x, 256, 9, y, 16, wk, NULL) == ERR_UNSUPPORTED      # batch > 8
     assert f(3, w, 16, 288, x, 288, 1, y, 16, wk, NULL) == ERR_SHAPE
     assert f(3, NULL, 0, 256, NULL, 256, 1, NULL, 0, NULL, NULL) == OK          # empty
+
+
+def test_gemv_float_validation():
+    lib = qblk.lib()
+    f = lib.qblk_gemv_float
+    w, x, y = _p(FAKE), _p(FAKE + 0x100000), _p(FAKE + 0x200000)
+    assert f(9, w, 16, 256, x, 256, 1, y, 16, NULL) == ERR_ARG                  # unknown type
+    assert f(3, w, 16, 288, x, 288, 1, y, 16, NULL) == ERR_SHAPE                # Q4_K k % 256
+    assert f(1, w, 16, 256, x, 255, 1, y, 16, NULL) == ERR_SHAPE                # ldx < k
+    assert f(1, w, 16, 256, x, 258, 1, y, 16, NULL) == ERR_ALIGN                # ldx % 4
+    assert f(1, w, 16, 256, _p(FAKE + 4), 256, 1, y, 16, NULL) == ERR_ALIGN     # x alignment
+    assert f(1, w, 16, 256, x, 256, 1, y, 15, NULL) == ERR_SHAPE                # ldy < n
+    assert f(1, NULL, 16, 256, x, 256, 1, y, 16, NULL) == ERR_ARG               # null wq
+    assert f(2, w, 16, 256, x, 256, 65, y, 16, NULL) == ERR_UNSUPPORTED         # batch > 64
+    assert f(3, NULL, 0, 256, NULL, 256, 1, NULL, 0, NULL) == OK                # empty
+    assert f(3, NULL, 16, 256, NULL, 256, 0, NULL, 16, NULL) == OK

@@ -397,3 +397,51 @@ def test_gemv_f32_strided_rows_and_limits():
     with pytest.raises(qblk.QblkError) as ei:
         qblk.qblk_gemv_f32(o.TYPE_Q4_K, wq9, 8, 256, x9)
     assert ei.value.status == -4
+
+
+# ================================================================ float activations
+
+def _float_expected(wtype, w, x):
+    _, enc = o.encode_weights(wtype, w)
+    return o.product_float(wtype, enc, x)[1]
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("n,k,batch", [(37, 1024, 1), (300, 4096, 2), (129, 2304, 3), (70, 256, 8),
+                                       (1000, 8192, 1), (65, 512, 11)])
+def test_gemv_float_random(wtype, n, k, batch):
+    print(f"gemv float {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
+    rng = np.random.default_rng(91 * wtype + n + batch)
+    w = _special_rows(rng, n, k)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    y = qblk.qblk_gemv_float(wtype, dev_pack(wtype, w), n, k, dev(x))
+    check_rel(host(y), _float_expected(wtype, w, x))
+
+
+@pytest.mark.parametrize("wtype", [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_0_F16])
+def test_gemv_float_ragged_blocks(wtype):
+    """k = 1056 (33 blocks: one chunk of 64 blocks, half the lanes idle) and a
+    strided activation (ldx > k) with a strided output (ldy > n)."""
+    print(f"gemv float ragged {TNAME[wtype]}", flush=True)
+    rng = np.random.default_rng(95 + wtype)
+    n, k, b = 45, 1056, 3
+    w = _special_rows(rng, n, k)
+    xbig = rng.standard_normal((b, k + 36)).astype(np.float32)
+    x = dev(xbig)[:, :k]
+    ybig = torch().full((b, n + 7), -5.0, device="cuda")
+    qblk.qblk_gemv_float(wtype, dev_pack(wtype, w), n, k, x, y=ybig[:, :n])
+    yh = host(ybig)
+    check_rel(yh[:, :n], _float_expected(wtype, w, xbig[:, :k]))
+    assert np.all(yh[:, n:] == -5.0)
+
+
+def test_gemv_float_full_size_sampled():
+    """Q4_K 14336 x 4096 and Q4_0 4096 x 4096 at the workload sizes, on sampled rows."""
+    for wl, wtype, n, k in ((3, o.TYPE_Q4_K, 14336, 4096), (1, o.TYPE_Q4_0, 4096, 4096)):
+        print(f"full-size gemv float {TNAME[wtype]} {n}x{k}", flush=True)
+        w = synth.weights(wl, 0, n, k)
+        x = synth.act(wl, 1, k)
+        wq = qblk.qblk_pack_weights(wtype, dev(w))
+        y = host(qblk.qblk_gemv_float(wtype, wq, n, k, dev(x)))
+        rows = _sample_rows(n, 64, n + 7)
+        check_rel(y[:, rows], _float_expected(wtype, w[rows], x))

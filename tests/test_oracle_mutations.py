@@ -154,3 +154,25 @@ def test_mutant_q4_0_f16_truncated_scale_is_caught(monkeypatch):
     monkeypatch.setattr(o, "fp16_round", trunc16)
     with pytest.raises(AssertionError):
         pins.test_q4_0_f16_scale_is_nearest_half_of_amax_over_7()
+
+
+def test_mutant_float_product_without_offset_8_is_caught(monkeypatch):
+    """The float product decoding Q4_0 nibbles without the offset of 8."""
+    def no_offset(wtype, enc, x):
+        deq = (np.asarray(enc["q"], np.float64) + 8) * np.repeat(np.asarray(enc["d"], np.float64), 32, axis=1)
+        y = np.asarray(x, np.float64) @ deq.T
+        return y.astype(np.float32), y
+    monkeypatch.setattr(o, "product_float", no_offset)
+    with pytest.raises(AssertionError):
+        pins.test_float_product_matches_page_decoders(o.TYPE_Q4_0)
+
+
+def test_mutant_float_product_dropped_q4_k_min_is_caught(monkeypatch):
+    def no_min(wtype, enc, x):
+        scale, _ = o.q4_k_sub_scales(enc)
+        deq = np.asarray(enc["q"], np.float64) * np.repeat(scale, 32, axis=1)
+        y = np.asarray(x, np.float64) @ deq.T
+        return y.astype(np.float32), y
+    monkeypatch.setattr(o, "product_float", no_min)
+    with pytest.raises(AssertionError):
+        pins.test_float_product_matches_page_decoders(o.TYPE_Q4_K)

@@ -224,3 +224,115 @@ def test_f16_ceil_div_brute_force():
         for vi, gi in zip(v, got):
             ok = np.nonzero(c * allvals >= vi)[0]
             assert gi == allbits[ok[0]], (c, vi)
+
+
+# ---------------------------------------------------------------- float-activation product
+
+def _page_q4_0_f16_float_dot(packed_row, K, yf):
+    """The runguoli page §6.4 scalar kernel reading the page's fp16 scales."""
+    nb = K // 32
+    scales = packed_row[:2 * nb].copy().view("<f2")
+    qs = packed_row[o.header_bytes(o.TYPE_Q4_0_F16, K):]
+    total = 0.0
+    for blk in range(nb):
+        scale = float(scales[blk])
+        for j in range(16):
+            byte = int(qs[16 * blk + j])
+            total += (((byte & 0x0F) - 8) * scale) * float(yf[32 * blk + 2 * j])
+            total += (((byte >> 4) - 8) * scale) * float(yf[32 * blk + 2 * j + 1])
+    return total
+
+
+def _page_q8_0_float_dot(packed_row, K, yf):
+    """Q8_0 (runguoli page §5.4: one fp32 scale, 32 int8 per block) decoded
+    from the library's row: the 8 codes of each group are stored as elements
+    0,2,4,6,1,3,5,7."""
+    nb = K // 32
+    scales = packed_row[:4 * nb].copy().view("<f4")
+    qs = packed_row[o.header_bytes(o.TYPE_Q8_0, K):].copy().view(np.int8)
+    order = (0, 2, 4, 6, 1, 3, 5, 7)
+    total = 0.0
+    for blk in range(nb):
+        for p in range(32):
+            g, pos = divmod(p, 8)
+            total += (int(qs[32 * blk + p]) * float(scales[blk])) * float(yf[32 * blk + 8 * g + order[pos]])
+    return total
+
+
+def _page_q4_k_float_dot(packed_row, K, yf):
+    """Q4_K (runguoli page §5.5: weight = q * (d * scale_j) + d_min * min_j)
+    decoded from the library's row: per super-block a header of fp16 d, fp16
+    d_min and a 96-bit field with 6-bit sc_j at bit 6j and mn_j at bit
+    48 + 6j, then 8 x 16 bytes whose byte t of sub-block j holds elements 2t
+    (low nibble) and 2t + 1 (high nibble)."""
+    nsb = K // 256
+    hdr = packed_row[:16 * nsb]
+    qs = packed_row[16 * nsb:]
+    total = 0.0
+    for sb in range(nsb):
+        h = hdr[16 * sb:16 * sb + 16]
+        d = float(h[0:2].copy().view("<f2")[0])
+        dmin = float(h[2:4].copy().view("<f2")[0])
+        field = int.from_bytes(bytes(h[4:16]), "little")
+        for j in range(8):
+            sc = (field >> (6 * j)) & 63
+            mn = (field >> (48 + 6 * j)) & 63
+            for t in range(16):
+                byte = int(qs[128 * sb + 16 * j + t])
+                for e, q in ((2 * t, byte & 0x0F), (2 * t + 1, byte >> 4)):
+                    total += (q * (d * sc) + dmin * mn) * float(yf[256 * sb + 32 * j + e])
+    return total
+
+
+_PAGE_FLOAT_DOT = {o.TYPE_Q4_0: _page_q4_0_float_dot, o.TYPE_Q8_0: _page_q8_0_float_dot,
+                   o.TYPE_Q4_K: _page_q4_k_float_dot, o.TYPE_Q4_0_F16: _page_q4_0_f16_float_dot}
+
+
+@pytest.mark.parametrize("wtype", [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K, o.TYPE_Q4_0_F16])
+def test_float_product_matches_page_decoders(wtype):
+    """product_float against the pages' decoders restated over the packed
+    bytes, element by element (no shared code with the oracle's unpackers)."""
+    rng = np.random.default_rng(60 + wtype)
+    N, M, K = 3, 2, 512
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[0, 40:80] = np.abs(w[0, 40:80])  # a sub-block with a zero point of 0
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    packed, enc = o.encode_weights(wtype, w)
+    y32, y64 = o.product_float(wtype, enc, x)
+    assert y64.shape == (M, N)
+    for m in range(M):
+        for n in range(N):
+            ref = _PAGE_FLOAT_DOT[wtype](packed[n], K, x[m].astype(np.float64))
+            assert abs(y64[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+            assert y32[m, n] == np.float32(y64[m, n])
+
+
+@pytest.mark.parametrize("wtype", [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_K, o.TYPE_Q4_0_F16])
+def test_float_product_on_dequantized_activations_is_the_quantized_product(wtype):
+    """With x = the dequantized Q8 activations (exact in fp64), the float
+    product and the integer-block product are the same sum, regrouped."""
+    rng = np.random.default_rng(70 + wtype)
+    N, M, K = 5, 3, 768
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    _, enc = o.encode_weights(wtype, w)
+    aq, da, sa = o.quantize_act(x)
+    xdeq = np.asarray(aq, np.float64) * np.repeat(np.asarray(da, np.float64), 32, axis=1)
+    yf = o.product_float(wtype, enc, xdeq)[1]
+    yq = o.product(wtype, enc, (aq, da, sa))[1]
+    assert np.max(np.abs(yf - yq)) <= 1e-12 * np.max(np.abs(yq))
+
+
+def test_float_product_unit_activation_picks_a_weight_column():
+    """x = e_k gives column k of the decoded weights, for every k of a block
+    (catches a transposed or shifted activation index)."""
+    rng = np.random.default_rng(80)
+    K = 256
+    w = (rng.standard_normal((2, K)) * 0.02).astype(np.float32)
+    packed, enc = o.encode_weights(o.TYPE_Q4_K, w)
+    deq = o.dequant_weights(o.TYPE_Q4_K, enc)
+    for kk in (0, 1, 31, 32, 255):
+        x = np.zeros((1, K), np.float32)
+        x[0, kk] = 1.0
+        assert np.array_equal(o.product_float(o.TYPE_Q4_K, enc, x)[1][0], deq[:, kk])
+        assert _page_q4_k_float_dot(packed[1], K, x[0].astype(np.float64)) == deq[1, kk]
