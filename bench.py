@@ -277,6 +277,7 @@ def main():
         secondary["layer_7b"] = layer_7b(torch, qblk, synth, dev, args)
         secondary["gemm"] = gemm_bench(torch, qblk, synth, dev, args.gemm_iters)
         secondary["q4_0_q8_0"] = sym_bench(torch, qblk, synth, dev)
+        secondary["kv_scores"] = kv_bench(torch, qblk, synth, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -512,6 +513,40 @@ def sym_bench(torch, qblk, synth, dev):
         res[fname] = {"us": round(us, 3), "weight_bytes": wb, "GBps": round(wb / (us * 1e-6) / 1e9, 1)}
         log(f"{fname}: {res[fname]}")
         del wqs
+        torch.cuda.empty_cache()
+    return res
+
+
+def kv_bench(torch, qblk, synth, dev):
+    """Scores of one decode step against a quantized K cache: 70B-shaped
+    (64 query heads over 8 KV heads of 128, 8192 cached tokens) and the
+    7B example of the KV-cache size formula (32 heads of 128, 2048 tokens),
+    one launch per layer, rotated over enough layers' caches to exceed the
+    last-level cache."""
+    res = {}
+    for name, t, n_kv, n_head, n_ctx in (("q8_0_70b_ctx8192", qblk.Q8_0, 8, 64, 8192),
+                                         ("q4_0_70b_ctx8192", qblk.Q4_0, 8, 64, 8192),
+                                         ("q8_0_7b_ctx2048", qblk.Q8_0, 32, 32, 2048)):
+        hd = 128
+        cb = qblk.qblk_kv_cache_bytes(t, n_kv, n_ctx, hd)
+        copies = max(2, int(600e6 // cb) + 1)
+        caches = []
+        for c in range(copies):
+            cache = qblk.qblk_kv_cache(t, n_kv, n_ctx, hd, device=dev)
+            k = synth.torch_activations(7000 + c, n_kv * n_ctx, hd, device=dev)
+            qblk.qblk_pack_weights(t, k, out=cache)  # rows (h, t) in order
+            caches.append(cache)
+            del k
+        qq = qblk.qblk_quantize_act(synth.torch_activations(7999, n_head, hd, device=dev))
+        s = torch.empty((n_head, n_ctx), dtype=torch.float32, device=dev)
+        us = timed_launches(torch, lambda i: qblk.qblk_kv_scores(t, caches[i % copies], n_kv, n_ctx, n_ctx, hd,
+                                                                  qq, n_head, scores=s), 100)
+        alg = cb + qblk.qblk_act_bytes(n_head, hd) + 4 * n_head * n_ctx
+        res[name] = {"us": round(us, 3), "cache_bytes": cb, "alg_bytes": alg,
+                     "cache_GBps": round(cb / (us * 1e-6) / 1e9, 1),
+                     "GBps": round(alg / (us * 1e-6) / 1e9, 1)}
+        log(f"kv scores {name}: {res[name]}")
+        del caches
         torch.cuda.empty_cache()
     return res
 

@@ -27,6 +27,7 @@ SOURCES = [
     "gemm.hip",
     "gemm_small.hip",
     "block_sums.hip",
+    "kv.hip",
     "api.cpp",
 ]
 

@@ -94,7 +94,7 @@ QBLK_EXPORT int qblk_pack_weights(int type, const float* w, int64_t n, int64_t k
   if (!aligned(w, 16) || ldw % 4 != 0 || !aligned(wq, 16)) return QBLK_ERR_ALIGN;
   if (8 * n * (k / 32) > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
-  return finish(qblk::launch_pack_weights(type, w, n, k, ldw, wq, stream));
+  return finish(qblk::launch_pack_weights(type, w, n, k, ldw, wq, qblk::row_bytes(type, k), stream));
 }
 
 QBLK_EXPORT int qblk_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, void* xq,
@@ -170,6 +170,50 @@ QBLK_EXPORT int qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const 
     return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_gemm(type, wq, n, k, xq, m, y, ldy, stream));
+}
+
+namespace {
+
+bool valid_kv(int type, int64_t head_dim) {
+  return (type == QBLK_Q4_0 || type == QBLK_Q8_0 || type == QBLK_Q4_0_F16) &&
+         (head_dim == 64 || head_dim == 128 || head_dim == 256);
+}
+
+}  // namespace
+
+QBLK_EXPORT size_t qblk_kv_cache_bytes(int type, int64_t n_kv, int64_t n_ctx, int64_t head_dim) {
+  if (!valid_kv(type, head_dim) || n_kv <= 0 || n_ctx <= 0 || n_kv > 65535) return 0;
+  return static_cast<size_t>(n_kv * n_ctx * qblk::row_bytes(type, head_dim));
+}
+
+QBLK_EXPORT int qblk_kv_store(int type, const float* x, int64_t n_kv, int64_t head_dim, int64_t ldx,
+                              void* cache, int64_t n_ctx, int64_t pos, hipStream_t stream) {
+  if (!(type == QBLK_Q4_0 || type == QBLK_Q8_0 || type == QBLK_Q4_0_F16) || n_kv < 0) return QBLK_ERR_ARG;
+  if (!valid_kv(type, head_dim) || n_ctx <= 0 || pos < 0 || pos >= n_ctx) return QBLK_ERR_SHAPE;
+  if (n_kv == 0) return QBLK_OK;
+  if (x == nullptr || cache == nullptr) return QBLK_ERR_ARG;
+  if (ldx < head_dim) return QBLK_ERR_SHAPE;
+  if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(cache, 16)) return QBLK_ERR_ALIGN;
+  if (n_kv > 65535) return QBLK_ERR_UNSUPPORTED;
+  const int64_t rb = qblk::row_bytes(type, head_dim);
+  (void)hipGetLastError();
+  return finish(qblk::launch_pack_weights(type, x, n_kv, head_dim, ldx, static_cast<uint8_t*>(cache) + pos * rb,
+                                          n_ctx * rb, stream));
+}
+
+QBLK_EXPORT int qblk_kv_scores(int type, const void* cache, int64_t n_kv, int64_t n_ctx, int64_t n_tok,
+                               int64_t head_dim, const void* q, int64_t n_head, float* scores, int64_t lds,
+                               hipStream_t stream) {
+  if (!(type == QBLK_Q4_0 || type == QBLK_Q8_0 || type == QBLK_Q4_0_F16)) return QBLK_ERR_ARG;
+  if (n_kv <= 0 || n_head <= 0 || n_head % n_kv != 0) return QBLK_ERR_ARG;
+  if (!valid_kv(type, head_dim) || n_ctx <= 0 || n_tok < 0 || n_tok > n_ctx) return QBLK_ERR_SHAPE;
+  if (n_tok == 0) return QBLK_OK;
+  if (cache == nullptr || q == nullptr || scores == nullptr) return QBLK_ERR_ARG;
+  if (lds < n_tok) return QBLK_ERR_SHAPE;
+  if (!aligned(cache, 16) || !aligned(q, 16) || !aligned(scores, 4)) return QBLK_ERR_ALIGN;
+  if (n_head / n_kv > 8 || n_kv > 65535) return QBLK_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(qblk::launch_kv_scores(type, cache, n_kv, n_ctx, n_tok, head_dim, q, n_head, scores, lds, stream));
 }
 
 QBLK_EXPORT int qblk_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,

@@ -38,7 +38,7 @@ __device__ __forceinline__ uint2 pack_group8(const int (&q)[8]) {
 template <int QMAX, bool F16 = false>
 __global__ __launch_bounds__(256) void pack_sym_kernel(const float* __restrict__ w, int64_t n,
                                                        int64_t k, int64_t ldw,
-                                                       uint8_t* __restrict__ wq, int64_t rb,
+                                                       uint8_t* __restrict__ wq, int64_t ob,
                                                        int64_t hb) {
   const int64_t nb = k / 32;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void pack_sym_kernel(const float* __restrict__
     q[i] = qi;
   }
 
-  uint8_t* dst = wq + row * rb;
+  uint8_t* dst = wq + row * ob;  // ob: bytes between output rows
   if constexpr (F16) {
     if (sub == 0) *reinterpret_cast<_Float16*>(dst + 2 * blk) = d16;
     // zero the padding at the end of the header region (up to 7 halves)
@@ -150,7 +150,7 @@ __device__ __forceinline__ double group8_max(double v, int lane) {
 // Eight lanes per super-block, lane j owns sub-block j (32 elements).
 __global__ __launch_bounds__(256) void pack_q4k_kernel(const float* __restrict__ w, int64_t n,
                                                        int64_t k, int64_t ldw,
-                                                       uint8_t* __restrict__ wq, int64_t rb,
+                                                       uint8_t* __restrict__ wq, int64_t ob,
                                                        int64_t hb) {
   const int64_t nsb = k / 256;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void pack_q4k_kernel(const float* __restrict__
     // byte t = i/2 of the sub-block: element 2t low nibble, 2t+1 high nibble
     nib[i >> 3] |= static_cast<uint32_t>(q) << (4 * (i & 7));
   }
-  uint8_t* dst = wq + row * rb;
+  uint8_t* dst = wq + row * ob;  // ob: bytes between output rows
   *reinterpret_cast<uint4*>(dst + hb + 128 * sb + 16 * j) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
 
   // assemble the 96-bit sc/mn field in lane j == 0 of the group
@@ -242,8 +242,8 @@ __global__ __launch_bounds__(256) void pack_q4k_kernel(const float* __restrict__
 }  // namespace
 
 hipError_t launch_pack_weights(int type, const float* w, int64_t n, int64_t k, int64_t ldw,
-                               void* wq, hipStream_t s) {
-  const int64_t rb = row_bytes(type, k);
+                               void* wq, int64_t out_stride, hipStream_t s) {
+  const int64_t rb = out_stride;
   const int64_t hb = header_bytes(type, k);
   uint8_t* out = static_cast<uint8_t*>(wq);
   if (type == kQ4_K) {

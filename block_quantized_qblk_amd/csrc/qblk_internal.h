@@ -38,8 +38,13 @@ inline int64_t row_bytes(int type, int64_t k) {
 // launch.
 hipError_t launch_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, void* xq,
                                hipStream_t s);
+// out_stride: bytes between output rows (row_bytes(type, k) for a dense matrix)
 hipError_t launch_pack_weights(int type, const float* w, int64_t n, int64_t k, int64_t ldw,
-                               void* wq, hipStream_t s);
+                               void* wq, int64_t out_stride, hipStream_t s);
+// Quantized KV cache: rows (h, t) of n_kv x n_ctx rows of row_bytes(type, head_dim).
+hipError_t launch_kv_scores(int type, const void* cache, int64_t n_kv, int64_t n_ctx, int64_t n_tok,
+                            int64_t head_dim, const void* q, int64_t n_head, float* scores, int64_t lds,
+                            hipStream_t s);
 hipError_t launch_gemv(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t batch, float* y, int64_t ldy, hipStream_t s);
 // Fused quantize + GEMV (fp32 activations): up to 8 activation rows per

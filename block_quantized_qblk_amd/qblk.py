@@ -50,6 +50,9 @@ def _load():
         "qblk_gemv_f32_work_bytes": (ctypes.c_size_t, [i64, i64]),
         "qblk_gemv_f32": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp, vp]),
         "qblk_gemv_float": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]),
+        "qblk_kv_cache_bytes": (ctypes.c_size_t, [i32, i64, i64, i64]),
+        "qblk_kv_store": (i32, [i32, vp, i64, i64, i64, vp, i64, i64, vp]),
+        "qblk_kv_scores": (i32, [i32, vp, i64, i64, i64, i64, vp, i64, vp, i64, vp]),
         "qblk_block_sums": (i32, [i32, vp, i64, i64, vp, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -240,6 +243,56 @@ def qblk_gemv_float(wtype, wq, n, k, x, batch=None, y=None, stream=None):
                                    int(batch), _ptr(y), y.stride(0), _stream(stream)),
            "qblk_gemv_float")
     return y
+
+
+def qblk_kv_cache_bytes(wtype, n_kv, n_ctx, head_dim):
+    return int(_load().qblk_kv_cache_bytes(_type(wtype), int(n_kv), int(n_ctx), int(head_dim)))
+
+
+def qblk_kv_cache(wtype, n_kv, n_ctx, head_dim, device="cuda"):
+    """A zeroed uint8 device buffer holding an n_kv x n_ctx quantized cache."""
+    import torch
+    nbytes = qblk_kv_cache_bytes(wtype, n_kv, n_ctx, head_dim)
+    if nbytes == 0:
+        raise ValueError("invalid KV cache shape or type")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def qblk_kv_store(wtype, x, cache, n_ctx, pos, stream=None):
+    """Quantize x (float32 [n_kv, head_dim], rows with unit stride) into rows
+    (h, pos) of the cache."""
+    import torch
+    _require_cuda(x, "x", rows=True)
+    _require_cuda(cache, "cache")
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32 [n_kv, head_dim]")
+    n_kv, head_dim = x.shape
+    if cache.numel() < qblk_kv_cache_bytes(wtype, n_kv, n_ctx, head_dim):
+        raise ValueError("cache smaller than qblk_kv_cache_bytes")
+    _check(_load().qblk_kv_store(_type(wtype), _ptr(x), int(n_kv), int(head_dim), x.stride(0), _ptr(cache),
+                                 int(n_ctx), int(pos), _stream(stream)), "qblk_kv_store")
+    return cache
+
+
+def qblk_kv_scores(wtype, cache, n_kv, n_ctx, n_tok, head_dim, q, n_head, scores=None, stream=None):
+    """float32 [n_head, n_tok] scores of the quantized queries q (activation
+    buffer of n_head rows of head_dim) against tokens [0, n_tok) of the cache."""
+    import torch
+    _require_cuda(cache, "cache")
+    _require_cuda(q, "q")
+    if cache.numel() < qblk_kv_cache_bytes(wtype, n_kv, n_ctx, head_dim):
+        raise ValueError("cache smaller than qblk_kv_cache_bytes")
+    if q.numel() < qblk_act_bytes(n_head, head_dim):
+        raise ValueError("q smaller than qblk_act_bytes(n_head, head_dim)")
+    if scores is None:
+        scores = torch.empty((n_head, max(int(n_tok), 1)), dtype=torch.float32, device=cache.device)
+    _require_cuda(scores, "scores", rows=True)
+    if scores.dtype != torch.float32 or scores.shape[0] < n_head or scores.shape[1] < n_tok:
+        raise ValueError("scores must be float32 [n_head, >= n_tok]")
+    _check(_load().qblk_kv_scores(_type(wtype), _ptr(cache), int(n_kv), int(n_ctx), int(n_tok), int(head_dim),
+                                  _ptr(q), int(n_head), _ptr(scores), scores.stride(0), _stream(stream)),
+           "qblk_kv_scores")
+    return scores
 
 
 def qblk_gemm(wtype, wq, n, k, xq, m, y=None, stream=None):

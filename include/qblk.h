@@ -224,6 +224,49 @@ int qblk_gemm(int type, const void *wq, int64_t n, int64_t k, const void *xq,
               int64_t m, float *y, int64_t ldy, hipStream_t stream);
 
 /*
+ * Quantized KV cache ("llama.cpp 推理引擎", §3.7.1: the cache keeps K and V of
+ * every earlier token so that a decode step computes only the new token's;
+ * §3.7.3: the cache may be stored as Q8_0 or Q4_0). Types QBLK_Q4_0,
+ * QBLK_Q8_0 and QBLK_Q4_0_F16; head_dim 64, 128 or 256.
+ *
+ * Layout: n_kv heads x n_ctx token rows; row (h, t) is the packed weight row
+ * (same layout and encoding as qblk_pack_weights) of the head_dim values of
+ * head h at token t, at byte (h * n_ctx + t) * qblk_weight_row_bytes(type,
+ * head_dim). The cache is owned by the caller; qblk_kv_cache_bytes gives its
+ * size (0 for an invalid type, head_dim, n_kv or n_ctx, or n_kv > 65535).
+ */
+size_t qblk_kv_cache_bytes(int type, int64_t n_kv, int64_t n_ctx, int64_t head_dim);
+
+/*
+ * Store one token: quantize x[h*ldx + i] (h < n_kv, i < head_dim; fp32,
+ * 16-byte aligned, ldx a multiple of 4) into rows (h, pos) of the cache, with
+ * the qblk_pack_weights rules. The same call serves a K cache and a V cache.
+ * Errors: QBLK_ERR_ARG (type, n_kv < 0, null pointers), QBLK_ERR_SHAPE
+ * (head_dim, n_ctx <= 0, pos outside [0, n_ctx), ldx < head_dim),
+ * QBLK_ERR_ALIGN, QBLK_ERR_UNSUPPORTED (n_kv > 65535), QBLK_ERR_LAUNCH.
+ */
+int qblk_kv_store(int type, const float *x, int64_t n_kv, int64_t head_dim, int64_t ldx,
+                  void *cache, int64_t n_ctx, int64_t pos, hipStream_t stream);
+
+/*
+ * Attention scores against a quantized K cache, the quantized QK^T of a
+ * decode step: for query head hq < n_head and token t < n_tok,
+ *   scores[hq*lds + t] = sum over 32-blocks j of dk[h][t][j] * dq[hq][j] * S
+ * with h = hq / (n_head / n_kv) (grouped queries share a KV head), dk the
+ * key block scale, dq the query block scale and S the integer dot of the key
+ * codes (Q4_0 / Q4_0_F16: nibble - 8) with the query codes. q is an
+ * activation buffer of n_head rows of head_dim (qblk_quantize_act).
+ * Accumulation is fp32. No scaling by 1/sqrt(head_dim) and no softmax.
+ * Errors: QBLK_ERR_ARG (type, n_kv or n_head <= 0, n_head % n_kv != 0, null
+ * pointers), QBLK_ERR_SHAPE (head_dim, n_ctx <= 0, n_tok outside [0, n_ctx],
+ * lds < n_tok), QBLK_ERR_ALIGN (cache, q: 16 bytes; scores: 4),
+ * QBLK_ERR_UNSUPPORTED (n_head / n_kv > 8, n_kv > 65535), QBLK_ERR_LAUNCH.
+ */
+int qblk_kv_scores(int type, const void *cache, int64_t n_kv, int64_t n_ctx, int64_t n_tok,
+                   int64_t head_dim, const void *q, int64_t n_head, float *scores, int64_t lds,
+                   hipStream_t stream);
+
+/*
  * Test export: the integer block sums S[mm][nn][j] (int32, layout
  * [m][n][k/32]) that qblk_gemv / qblk_gemm scale and accumulate, computed
  * with the same device unpack and dot code. Intended for small shapes.

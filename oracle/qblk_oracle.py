@@ -625,6 +625,31 @@ def dequant_weights(wtype, enc):
     return dequant_q4_k(enc)
 
 
+# --------------------------------------------------------------------------
+# quantized KV cache ([P2] §3.7.1 K/V of earlier tokens are kept; §3.7.3 the
+# cache may be stored as Q8_0 or Q4_0)
+# --------------------------------------------------------------------------
+
+def kv_scores(wtype, k, q, n_head):
+    """Scores of n_head queries against a quantized K cache.
+
+    k: fp32 [n_kv, n_tok, head_dim], the keys of every cached token, each
+    token's head_dim values quantized like one weight row of type wtype.
+    q: fp32 [n_head, head_dim], quantized like activations (R3).
+    Query head hq reads KV head h = hq // (n_head // n_kv) (grouped queries).
+    scores[hq, t] is the weight-product of key row (h, t) with query hq.
+    Returns (y32, y64), shape [n_head, n_tok]."""
+    k = np.asarray(k, np.float32)
+    n_kv, n_tok, _ = k.shape
+    group = n_head // n_kv
+    aq, da, sa = quantize_act(q)
+    y = np.zeros((n_head, n_tok), np.float64)
+    for hq in range(n_head):
+        _, enc = encode_weights(wtype, k[hq // group])
+        y[hq] = product(wtype, enc, (aq[hq:hq + 1], da[hq:hq + 1], sa[hq:hq + 1]))[1][0]
+    return y.astype(np.float32), y
+
+
 def rel_err(y, yref):
     """max |y - yref| / max |yref| over the whole output (0 if both are 0)."""
     y = np.asarray(y, np.float64)

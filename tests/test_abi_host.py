@@ -170,3 +170,35 @@ def test_gemv_float_validation():
     assert f(2, w, 16, 256, x, 256, 65, y, 16, NULL) == ERR_UNSUPPORTED         # batch > 64
     assert f(3, NULL, 0, 256, NULL, 256, 1, NULL, 0, NULL) == OK                # empty
     assert f(3, NULL, 16, 256, NULL, 256, 0, NULL, 16, NULL) == OK
+
+
+def test_kv_cache_validation():
+    for t in (o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_0_F16):
+        for hd in (64, 128, 256):
+            assert qblk.qblk_kv_cache_bytes(t, 8, 1000, hd) == 8 * 1000 * o.row_bytes(t, hd)
+    assert qblk.qblk_kv_cache_bytes(o.TYPE_Q4_K, 8, 1000, 256) == 0
+    assert qblk.qblk_kv_cache_bytes(o.TYPE_Q8_0, 8, 1000, 96) == 0
+    assert qblk.qblk_kv_cache_bytes(o.TYPE_Q8_0, 0, 1000, 128) == 0
+    assert qblk.qblk_kv_cache_bytes(o.TYPE_Q8_0, 8, 0, 128) == 0
+    lib = qblk.lib()
+    x, c, q, s = _p(FAKE), _p(FAKE + 0x100000), _p(FAKE + 0x200000), _p(FAKE + 0x300000)
+    st = lib.qblk_kv_store
+    assert st(3, x, 8, 128, 128, c, 100, 0, NULL) == ERR_ARG                  # Q4_K
+    assert st(2, x, 8, 96, 96, c, 100, 0, NULL) == ERR_SHAPE                  # head_dim
+    assert st(2, x, 8, 128, 128, c, 100, 100, NULL) == ERR_SHAPE              # pos == n_ctx
+    assert st(2, x, 8, 128, 128, c, 100, -1, NULL) == ERR_SHAPE
+    assert st(2, x, 8, 128, 127, c, 100, 0, NULL) == ERR_SHAPE                # ldx < head_dim
+    assert st(2, x, 8, 128, 130, c, 100, 0, NULL) == ERR_ALIGN                # ldx % 4
+    assert st(2, x, 8, 128, 128, _p(FAKE + 8), 100, 0, NULL) == ERR_ALIGN
+    assert st(2, NULL, 8, 128, 128, c, 100, 0, NULL) == ERR_ARG
+    assert st(2, NULL, 0, 128, 128, NULL, 100, 0, NULL) == OK                 # no heads
+    sc = lib.qblk_kv_scores
+    assert sc(3, c, 8, 100, 10, 128, q, 64, s, 10, NULL) == ERR_ARG          # Q4_K
+    assert sc(2, c, 8, 100, 10, 128, q, 60, s, 10, NULL) == ERR_ARG          # n_head % n_kv
+    assert sc(2, c, 0, 100, 10, 128, q, 64, s, 10, NULL) == ERR_ARG
+    assert sc(2, c, 8, 100, 101, 128, q, 64, s, 101, NULL) == ERR_SHAPE      # n_tok > n_ctx
+    assert sc(2, c, 8, 100, 10, 128, q, 64, s, 9, NULL) == ERR_SHAPE         # lds < n_tok
+    assert sc(2, c, 8, 100, 10, 128, _p(FAKE + 4), 64, s, 10, NULL) == ERR_ALIGN
+    assert sc(2, c, 8, 100, 10, 128, q, 64, _p(FAKE + 2), 10, NULL) == ERR_ALIGN
+    assert sc(2, c, 4, 100, 10, 128, q, 64, s, 10, NULL) == ERR_UNSUPPORTED  # group 16
+    assert sc(2, NULL, 8, 100, 0, 128, NULL, 64, NULL, 0, NULL) == OK        # no tokens

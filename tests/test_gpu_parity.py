@@ -445,3 +445,91 @@ def test_gemv_float_full_size_sampled():
         y = host(qblk.qblk_gemv_float(wtype, wq, n, k, dev(x)))
         rows = _sample_rows(n, 64, n + 7)
         check_rel(y[:, rows], _float_expected(wtype, w[rows], x))
+
+
+# ================================================================ quantized KV cache
+
+KV_TYPES = [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_0_F16]
+
+
+def _kv_fill(wtype, k, n_ctx):
+    """Device cache holding k [n_kv, n_tok, hd] in rows (h, t), written per
+    head with the weight packer (a prefill's bulk write)."""
+    n_kv, n_tok, hd = k.shape
+    cache = qblk.qblk_kv_cache(wtype, n_kv, n_ctx, hd)
+    rb = qblk.qblk_weight_row_bytes(wtype, hd)
+    for h in range(n_kv):
+        view = cache[h * n_ctx * rb:(h * n_ctx + n_tok) * rb]
+        qblk.qblk_pack_weights(wtype, dev(k[h]), out=view)
+    return cache
+
+
+@pytest.mark.parametrize("wtype", KV_TYPES)
+def test_kv_store_bit_exact(wtype):
+    """Token-by-token stores land in rows (h, pos) with the packer's bytes;
+    rows not written stay untouched."""
+    print(f"kv store {TNAME[wtype]}", flush=True)
+    rng = np.random.default_rng(120 + wtype)
+    n_kv, n_ctx, n_tok, hd = 3, 40, 29, 128
+    k = rng.standard_normal((n_kv, n_tok, hd)).astype(np.float32)
+    k[1, 3] = 0.0
+    cache = qblk.qblk_kv_cache(wtype, n_kv, n_ctx, hd)
+    for t in range(n_tok):
+        qblk.qblk_kv_store(wtype, dev(np.ascontiguousarray(k[:, t])), cache, n_ctx, t)
+    got = host(cache).reshape(n_kv, n_ctx, -1)
+    for h in range(n_kv):
+        ref, _ = o.encode_weights(wtype, k[h])
+        assert np.array_equal(got[h, :n_tok], ref)
+        assert np.all(got[h, n_tok:] == 0)
+
+
+@pytest.mark.parametrize("wtype", KV_TYPES)
+@pytest.mark.parametrize("n_kv,n_head,hd,n_ctx,n_tok", [(1, 1, 128, 64, 1), (2, 8, 128, 300, 257),
+                                                        (4, 8, 64, 100, 100), (2, 16, 256, 50, 33),
+                                                        (3, 6, 128, 80, 45)])
+def test_kv_scores_random(wtype, n_kv, n_head, hd, n_ctx, n_tok):
+    print(f"kv scores {TNAME[wtype]} n_kv={n_kv} n_head={n_head} hd={hd} n_tok={n_tok}", flush=True)
+    rng = np.random.default_rng(130 + wtype + n_tok)
+    k = rng.standard_normal((n_kv, n_tok, hd)).astype(np.float32)
+    k[0, 0, :32] = 0.0
+    q = rng.standard_normal((n_head, hd)).astype(np.float32)
+    cache = _kv_fill(wtype, k, n_ctx)
+    s = torch().full((n_head, n_tok + 5), -9.0, device="cuda")
+    qblk.qblk_kv_scores(wtype, cache, n_kv, n_ctx, n_tok, hd, dev_quantize(q), n_head, scores=s[:, :n_tok])
+    sh = host(s)
+    check_rel(sh[:, :n_tok], o.kv_scores(wtype, k, q, n_head)[1])
+    assert np.all(sh[:, n_tok:] == -9.0)
+
+
+def test_kv_scores_prefix_and_stores_agree():
+    """Scores over a prefix of the cache, after token-by-token stores, equal
+    the oracle's on that prefix; an empty prefix writes nothing."""
+    print("kv scores prefix", flush=True)
+    rng = np.random.default_rng(140)
+    n_kv, n_head, hd, n_ctx, n_tok = 2, 4, 128, 64, 50
+    k = rng.standard_normal((n_kv, n_tok, hd)).astype(np.float32)
+    q = rng.standard_normal((n_head, hd)).astype(np.float32)
+    cache = qblk.qblk_kv_cache(o.TYPE_Q8_0, n_kv, n_ctx, hd)
+    for t in range(n_tok):
+        qblk.qblk_kv_store(o.TYPE_Q8_0, dev(np.ascontiguousarray(k[:, t])), cache, n_ctx, t)
+    qq = dev_quantize(q)
+    for prefix in (1, 17, 50):
+        s = qblk.qblk_kv_scores(o.TYPE_Q8_0, cache, n_kv, n_ctx, prefix, hd, qq, n_head)
+        check_rel(host(s)[:, :prefix], o.kv_scores(o.TYPE_Q8_0, k[:, :prefix], q, n_head)[1])
+    s = torch().full((n_head, 4), -1.0, device="cuda")
+    qblk.qblk_kv_scores(o.TYPE_Q8_0, cache, n_kv, n_ctx, 0, hd, qq, n_head, scores=s)
+    assert np.all(host(s) == -1.0)
+
+
+def test_kv_scores_70b_shape_sampled():
+    """70B-shaped decode step: 64 query heads over 8 KV heads of 128, 8192
+    cached tokens, Q8_0; the oracle checks sampled tokens of every head."""
+    print("kv scores 70B shape", flush=True)
+    rng = np.random.default_rng(150)
+    n_kv, n_head, hd, n_ctx = 8, 64, 128, 8192
+    k = rng.standard_normal((n_kv, n_ctx, hd)).astype(np.float32)
+    q = rng.standard_normal((n_head, hd)).astype(np.float32)
+    cache = _kv_fill(o.TYPE_Q8_0, k, n_ctx)
+    s = host(qblk.qblk_kv_scores(o.TYPE_Q8_0, cache, n_kv, n_ctx, n_ctx, hd, dev_quantize(q), n_head))
+    toks = _sample_rows(n_ctx, 200, 151)
+    check_rel(s[:, toks], o.kv_scores(o.TYPE_Q8_0, k[:, toks], q, n_head)[1])

@@ -176,3 +176,19 @@ def test_mutant_float_product_dropped_q4_k_min_is_caught(monkeypatch):
     monkeypatch.setattr(o, "product_float", no_min)
     with pytest.raises(AssertionError):
         pins.test_float_product_matches_page_decoders(o.TYPE_Q4_K)
+
+
+def test_mutant_kv_head_interleaved_is_caught(monkeypatch):
+    """Query head hq reading KV head hq % n_kv instead of hq // group."""
+    def interleaved(wtype, k, q, n_head):
+        k = np.asarray(k, np.float32)
+        n_kv, n_tok, _ = k.shape
+        aq, da, sa = o.quantize_act(q)
+        y = np.zeros((n_head, n_tok), np.float64)
+        for hq in range(n_head):
+            _, enc = o.encode_weights(wtype, k[hq % n_kv])
+            y[hq] = o.product(wtype, enc, (aq[hq:hq + 1], da[hq:hq + 1], sa[hq:hq + 1]))[1][0]
+        return y.astype(np.float32), y
+    monkeypatch.setattr(o, "kv_scores", interleaved)
+    with pytest.raises(AssertionError):
+        pins.test_kv_scores_group_structure()

@@ -336,3 +336,37 @@ def test_float_product_unit_activation_picks_a_weight_column():
         x[0, kk] = 1.0
         assert np.array_equal(o.product_float(o.TYPE_Q4_K, enc, x)[1][0], deq[:, kk])
         assert _page_q4_k_float_dot(packed[1], K, x[0].astype(np.float64)) == deq[1, kk]
+
+
+# ---------------------------------------------------------------- quantized KV cache
+
+@pytest.mark.parametrize("wtype", [o.TYPE_Q4_0, o.TYPE_Q8_0, o.TYPE_Q4_0_F16])
+def test_kv_scores_match_page_decoders_with_grouped_heads(wtype):
+    """Each score is the pages' decoded key row times the dequantized query
+    (exact in fp64), with query head hq reading KV head hq // group."""
+    rng = np.random.default_rng(100 + wtype)
+    n_kv, n_head, n_tok, hd = 2, 6, 5, 64
+    k = rng.standard_normal((n_kv, n_tok, hd)).astype(np.float32)
+    q = rng.standard_normal((n_head, hd)).astype(np.float32)
+    y32, y64 = o.kv_scores(wtype, k, q, n_head)
+    assert y64.shape == (n_head, n_tok)
+    aq, da, _ = o.quantize_act(q)
+    qdeq = np.asarray(aq, np.float64) * np.repeat(np.asarray(da, np.float64), 32, axis=1)
+    for hq in range(n_head):
+        packed, _ = o.encode_weights(wtype, k[hq // 3])
+        for t in range(n_tok):
+            ref = _PAGE_FLOAT_DOT[wtype](packed[t], hd, qdeq[hq])
+            assert abs(y64[hq, t] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_kv_scores_group_structure():
+    """Equal queries in one group give equal rows; a zero KV head gives zero
+    scores for exactly its group."""
+    rng = np.random.default_rng(110)
+    n_kv, n_head, n_tok, hd = 2, 8, 7, 128
+    k = rng.standard_normal((n_kv, n_tok, hd)).astype(np.float32)
+    k[1] = 0.0
+    q = np.repeat(rng.standard_normal((1, hd)).astype(np.float32), n_head, axis=0)
+    y = o.kv_scores(o.TYPE_Q8_0, k, q, n_head)[1]
+    assert np.all(y[:4] == y[0]) and np.any(y[0] != 0.0)
+    assert np.all(y[4:] == 0.0)
