@@ -578,11 +578,13 @@ hipError_t launch_cfg(const Plan& p, hipStream_t s) {
 enum Mode { kQuantized = 0, kLdsFused = 1, kInLaunch = 2 };
 
 // Kernel variant per shape, from measurements on MI355X over the 7B- and
-// 70B-shaped Q4_K matrices (batch 1, graphs of back-to-back launches): the
+// 70B-shaped Q4_K matrices (graphs of back-to-back launches): at batch 1 the
 // classic kernel with 4 rows per wave streams the largest matrices best
 // (6.0-6.5 TB/s), with 2 rows per wave the mid-size ones (activations staged
-// in LDS), 1 row per wave with 2 chunks in flight the small ones. All
-// variants give bit-identical results.
+// in LDS), 1 row per wave with 2 chunks in flight the small ones; at batch
+// 2-8, 8 rows per wave above 16k rows and 4 above 3k (70B layer at batch 4:
+// 142 us against 179 us with 2 rows per wave). All variants give
+// bit-identical results.
 template <int TYPE, int B, int MODE>
 hipError_t launch_b(const Plan& p, hipStream_t s) {
   constexpr bool SYNC = MODE == kInLaunch;
@@ -599,7 +601,11 @@ hipError_t launch_b(const Plan& p, hipStream_t s) {
     if (n >= 3072) return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
     return launch_cfg<TYPE, 1, 1, 2, SYNC>(p, s);
   } else {
-    if (n >= 3072) return launch_cfg<TYPE, B, 2, 1, SYNC>(p, s);
+    // several activation rows: every row a wave owns re-uses the activation
+    // registers, and at batch 2-8 those re-reads bound the kernel, so the
+    // larger matrices take more rows per wave
+    if (n >= 16384) return launch_cfg<TYPE, B, 8, 1, SYNC>(p, s);
+    if (n >= 3072) return launch_cfg<TYPE, B, 4, 1, SYNC>(p, s);
     return launch_cfg<TYPE, B, 1, 1, SYNC>(p, s);
   }
 }

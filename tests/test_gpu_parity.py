@@ -205,7 +205,8 @@ def test_gemm_exact_arithmetic(wtype, m):
 
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("n,k,batch", [(37, 1024, 1), (300, 4096, 1), (129, 2304, 4),
-                                       (64, 256, 8), (70, 512, 64)])
+                                       (64, 256, 8), (70, 512, 64), (3100, 512, 2),
+                                       (16400, 512, 5)])
 def test_gemv_random(wtype, n, k, batch):
     print(f"gemv {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
     rng = np.random.default_rng(31 * wtype + n + batch)
@@ -329,6 +330,7 @@ def test_gemm_prefill_full_size_sampled(m):
 @pytest.mark.parametrize("n,k,batch", [(37, 1024, 1), (300, 4096, 3), (4100, 2304, 1),
                                        (9000, 8192, 1), (129, 4096, 6), (70, 256, 8),
                                        (2000, 28672, 1), (17000, 4096, 1), (8200, 16384, 1),
+                                       (16400, 4096, 3), (16384, 2048, 8),
                                        (5000, 28672, 4)])
 def test_gemv_f32_matches_quantize_then_gemv(wtype, n, k, batch):
     if wtype == o.TYPE_Q4_K and k % 256:
