@@ -278,6 +278,7 @@ def main():
         secondary["gemm"] = gemm_bench(torch, qblk, synth, dev, args.gemm_iters)
         secondary["q4_0_q8_0"] = sym_bench(torch, qblk, synth, dev)
         secondary["kv_scores"] = kv_bench(torch, qblk, synth, dev)
+        secondary["multi_qkv"] = multi_bench(torch, qblk, synth, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -514,6 +515,52 @@ def sym_bench(torch, qblk, synth, dev):
         log(f"{fname}: {res[fname]}")
         del wqs
         torch.cuda.empty_cache()
+    return res
+
+
+def multi_bench(torch, qblk, synth, dev):
+    """70B-shaped q, k, v projections (8192, 1024, 1024 rows of 8192) on one
+    quantized activation: three qblk_gemv launches, one qblk_gemv_multi
+    launch over the three matrices, and one qblk_gemv over the same rows
+    packed as one 10240-row matrix; rotated over enough layers' weights to
+    exceed the last-level cache."""
+    k = 8192
+    ns = (8192, 1024, 1024)
+    wb = sum(qblk.qblk_weight_bytes(qblk.Q4_K, n, k) for n in ns)
+    copies = max(2, int(600e6 // wb) + 1)
+    layers = []
+    for c in range(copies):
+        w = synth.torch_weights("student_t", 8100 + c, sum(ns), k, device=dev)
+        cat = qblk.qblk_pack_weights(qblk.Q4_K, w)
+        rb = qblk.qblk_weight_row_bytes(qblk.Q4_K, k)
+        parts, r0 = [], 0
+        for n in ns:
+            parts.append(cat[r0 * rb:(r0 + n) * rb])
+            r0 += n
+        layers.append((cat, parts))
+        del w
+    xq = qblk.qblk_quantize_act(synth.torch_activations(8199, 1, k, device=dev))
+    ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for n in ns]
+    ycat = torch.empty((1, sum(ns)), dtype=torch.float32, device=dev)
+
+    def separate(i):
+        for part, n, y in zip(layers[i % copies][1], ns, ys):
+            qblk.qblk_gemv(qblk.Q4_K, part, n, k, xq, 1, y=y)
+
+    def multi(i):
+        qblk.qblk_gemv_multi(qblk.Q4_K, [(part, n, k, xq, y) for part, n, y in zip(layers[i % copies][1], ns, ys)],
+                             1)
+
+    def concat(i):
+        qblk.qblk_gemv(qblk.Q4_K, layers[i % copies][0], sum(ns), k, xq, 1, y=ycat)
+
+    res = {"weight_bytes": wb}
+    for name, fn in (("three_launches", separate), ("multi_launch", multi), ("concatenated", concat)):
+        us = timed_launches(torch, fn, 60)
+        res[name] = {"us": round(us, 3), "GBps": round(wb / (us * 1e-6) / 1e9, 1)}
+    log(f"q/k/v as three matrices: {res}")
+    del layers
+    torch.cuda.empty_cache()
     return res
 
 

@@ -30,6 +30,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // A dispatch holds fewer than 2^32 work-items per grid dimension.
 constexpr int64_t kMaxGridThreads = (int64_t{1} << 32) - 256;
 
+static_assert(QBLK_GEMV_MULTI_MAX == qblk::kGemvMultiMax, "descriptor list sizes agree");
+
 int finish(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
@@ -143,6 +145,28 @@ QBLK_EXPORT int qblk_gemv_f32(int type, const void* wq, int64_t n, int64_t k, co
   if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, work, stream));
+}
+
+QBLK_EXPORT int qblk_gemv_multi(int type, const qblk_gemv_desc* descs, int count, int64_t batch,
+                                hipStream_t stream) {
+  if (!valid_type(type) || count < 0 || batch < 0) return QBLK_ERR_ARG;
+  if (count == 0 || batch == 0) return QBLK_OK;
+  if (descs == nullptr) return QBLK_ERR_ARG;
+  if (count > QBLK_GEMV_MULTI_MAX) return QBLK_ERR_UNSUPPORTED;
+  int64_t wgs = 0;
+  for (int i = 0; i < count; ++i) {
+    const qblk_gemv_desc& d = descs[i];
+    const int st = check_product(type, d.wq, d.n, d.k, d.xq, batch, d.y, d.ldy);
+    if (st != QBLK_OK) return st;
+    wgs += (d.n + 7) / 8;  // at most 2 rows per wave, 4 waves per workgroup
+  }
+  if (batch > QBLK_GEMV_MAX_BATCH) return QBLK_ERR_UNSUPPORTED;
+  if (256 * wgs > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  qblk::GemvDesc d[QBLK_GEMV_MULTI_MAX];
+  for (int i = 0; i < count; ++i)
+    d[i] = qblk::GemvDesc{descs[i].wq, descs[i].n, descs[i].k, descs[i].xq, descs[i].y, descs[i].ldy};
+  (void)hipGetLastError();
+  return finish(qblk::launch_gemv_multi(type, d, count, batch, stream));
 }
 
 QBLK_EXPORT int qblk_gemv_float(int type, const void* wq, int64_t n, int64_t k, const float* x,

@@ -266,12 +266,14 @@ __device__ __forceinline__ void load_act_block(const GemvArgs& g, const uint8_t*
 // SYNC: the activation is quantized inside the launch (produce /
 // wait_slices); ALDS: it is read from LDS (stage_acts). Either way the first
 // chunks' weight loads are issued before the wait / staging.
-template <int TYPE, int B, int R, int U, bool SYNC = false, bool ALDS = false>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
+// `block` is the workgroup's index within this product (blockIdx.x, or its
+// offset inside a descriptor's range for the multi-product launch).
+template <int TYPE, int B, int R, int U, bool SYNC, bool ALDS>
+__device__ __forceinline__ void gemv_body(const GemvArgs& g, uint32_t block) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr bool kAllWaves = SYNC || ALDS;  // workgroup barriers ahead: no early exit
   const uint32_t lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
+  const int64_t wave = static_cast<int64_t>(block) * kWavesPerBlock +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t row0 = wave * R;
   uint64_t tag = 0;
@@ -369,6 +371,31 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
       if (lane == 63 && row0 + r < g.n) g.y[b * g.ldy + row0 + r] = v;
     }
   }
+}
+
+template <int TYPE, int B, int R, int U, bool SYNC = false, bool ALDS = false>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
+  gemv_body<TYPE, B, R, U, SYNC, ALDS>(g, blockIdx.x);
+}
+
+// Several independent products in one launch (a descriptor list, e.g. the
+// q, k and v matrices of a layer kept as separate buffers): the workgroups
+// of descriptor i are [first[i], first[i+1]) and run the classic kernel on
+// it. Quantized activations only.
+struct GemvMulti {
+  GemvArgs d[kGemvMultiMax];
+  uint32_t first[kGemvMultiMax + 1];
+  int count;
+};
+
+template <int TYPE, int B, int R, int U, bool ALDS>
+__global__ __launch_bounds__(256) void gemv_multi_kernel(GemvMulti m) {
+  const uint32_t block = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int t = 1; t < kGemvMultiMax; ++t)
+    if (t < m.count && block >= m.first[t]) i = t;  // uniform
+  gemv_body<TYPE, B, R, U, false, ALDS>(m.d[i], block - m.first[i]);
 }
 
 // Pipelined variant: chunk c+1's weights (and, fused, its fp32 activations)
@@ -655,6 +682,85 @@ hipError_t launch_gemv(int type, const void* wq, int64_t n, int64_t k, const voi
     p.A.ds = full.ds + 8 * b0 * p.nb;
     p.y = y + b0 * ldy;
     const hipError_t e = launch_type<kQuantized>(type, bc, p, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+namespace {
+
+template <int TYPE, int B, int R, int U>
+hipError_t launch_multi_r(GemvMulti& m, const int64_t* rows, int count, int64_t max_nb, hipStream_t s) {
+  uint32_t blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    m.first[i] = blocks;
+    blocks += grid_for<R>(rows[i]).x;
+  }
+  for (int i = count; i <= kGemvMultiMax; ++i) m.first[i] = blocks;
+  m.count = count;
+  if (blocks == 0) return hipSuccess;
+  if (stage_in_lds(B, max_nb)) {
+    hipLaunchKernelGGL((gemv_multi_kernel<TYPE, B, R, U, true>), dim3(blocks), dim3(64 * kWavesPerBlock),
+                       act_lds_bytes(B, static_cast<uint32_t>(max_nb)), s, m);
+  } else {
+    hipLaunchKernelGGL((gemv_multi_kernel<TYPE, B, R, U, false>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s,
+                       m);
+  }
+  return hipGetLastError();
+}
+
+// rows per wave as for the mid-size single products: 2 at batch 1, 4 above
+template <int TYPE>
+hipError_t launch_multi_type(int b, GemvMulti& m, const int64_t* rows, int count, int64_t max_nb,
+                             hipStream_t s) {
+  switch (b) {
+    case 1: return launch_multi_r<TYPE, 1, 2, 1>(m, rows, count, max_nb, s);
+    case 2: return launch_multi_r<TYPE, 2, 4, 1>(m, rows, count, max_nb, s);
+    case 3: return launch_multi_r<TYPE, 3, 4, 1>(m, rows, count, max_nb, s);
+    case 4: return launch_multi_r<TYPE, 4, 4, 1>(m, rows, count, max_nb, s);
+    case 5: return launch_multi_r<TYPE, 5, 4, 1>(m, rows, count, max_nb, s);
+    case 6: return launch_multi_r<TYPE, 6, 4, 1>(m, rows, count, max_nb, s);
+    case 7: return launch_multi_r<TYPE, 7, 4, 1>(m, rows, count, max_nb, s);
+    default: return launch_multi_r<TYPE, 8, 4, 1>(m, rows, count, max_nb, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_multi(int type, const GemvDesc* d, int count, int64_t batch, hipStream_t s) {
+  for (int64_t b0 = 0; b0 < batch; b0 += 8) {
+    const int bc = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
+    GemvMulti m{};
+    int64_t rows[kGemvMultiMax];
+    int used = 0;
+    int64_t max_nb = 0;
+    for (int i = 0; i < count; ++i) {
+      if (d[i].n == 0) continue;
+      Plan p{};
+      p.W.base = static_cast<const uint8_t*>(d[i].wq);
+      p.W.row_bytes = row_bytes(type, d[i].k);
+      p.W.hdr_bytes = header_bytes(type, d[i].k);
+      p.n = d[i].n;
+      p.nb = d[i].k / 32;
+      const ActView full = make_act(d[i].xq, batch, d[i].k);
+      p.A = full;
+      p.A.q = full.q + b0 * d[i].k;
+      p.A.ds = full.ds + 8 * b0 * p.nb;
+      p.y = d[i].y + b0 * d[i].ldy;
+      p.ldy = d[i].ldy;
+      m.d[used] = make_args(p);
+      rows[used] = p.n;
+      max_nb = p.nb > max_nb ? p.nb : max_nb;
+      ++used;
+    }
+    if (used == 0) return hipSuccess;
+    hipError_t e;
+    switch (type) {
+      case kQ4_0: e = launch_multi_type<kQ4_0>(bc, m, rows, used, max_nb, s); break;
+      case kQ8_0: e = launch_multi_type<kQ8_0>(bc, m, rows, used, max_nb, s); break;
+      case kQ4_0H: e = launch_multi_type<kQ4_0H>(bc, m, rows, used, max_nb, s); break;
+      default: e = launch_multi_type<kQ4_K>(bc, m, rows, used, max_nb, s); break;
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -68,6 +68,17 @@ inline int64_t gemv_f32_work_bytes(int64_t batch, int64_t k) {
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
                            int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
                            hipStream_t s);
+// one product of a multi-product GEMV launch (quantized activations)
+struct GemvDesc {
+  const void* wq;
+  int64_t n;
+  int64_t k;
+  const void* xq;
+  float* y;
+  int64_t ldy;
+};
+constexpr int kGemvMultiMax = 16;
+hipError_t launch_gemv_multi(int type, const GemvDesc* d, int count, int64_t batch, hipStream_t s);
 hipError_t launch_gemv_float(int type, const void* wq, int64_t n, int64_t k, const float* x,
                              int64_t ldx, int64_t batch, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,

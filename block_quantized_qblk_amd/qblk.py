@@ -50,6 +50,7 @@ def _load():
         "qblk_gemv_f32_work_bytes": (ctypes.c_size_t, [i64, i64]),
         "qblk_gemv_f32": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp, vp]),
         "qblk_gemv_float": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]),
+        "qblk_gemv_multi": (i32, [i32, vp, i32, i64, vp]),
         "qblk_kv_cache_bytes": (ctypes.c_size_t, [i32, i64, i64, i64]),
         "qblk_kv_store": (i32, [i32, vp, i64, i64, i64, vp, i64, i64, vp]),
         "qblk_kv_scores": (i32, [i32, vp, i64, i64, i64, i64, vp, i64, vp, i64, vp]),
@@ -219,6 +220,34 @@ def qblk_gemv_f32(wtype, wq, n, k, x, batch=None, y=None, work=None, stream=None
                                  int(batch), _ptr(y), y.stride(0), _ptr(work), _stream(stream)),
            "qblk_gemv_f32")
     return y
+
+
+class GemvDesc(ctypes.Structure):
+    """One product of qblk_gemv_multi (mirrors qblk_gemv_desc)."""
+    _fields_ = [("wq", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("xq", ctypes.c_void_p), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
+def qblk_gemv_multi(wtype, products, batch, stream=None):
+    """Several qblk_gemv products in one launch. products: list of
+    (wq, n, k, xq, y) with y a float32 [>= batch, >= n] device tensor
+    (unit stride along rows). Returns the list of y."""
+    import torch
+    descs = (GemvDesc * max(1, len(products)))()
+    for i, (wq, n, k, xq, y) in enumerate(products):
+        _require_cuda(wq, "wq")
+        _require_cuda(xq, "xq")
+        _require_cuda(y, "y", rows=True)
+        if y.dtype != torch.float32 or y.shape[0] < batch or y.shape[1] < n:
+            raise ValueError("y must be float32 [batch, >= n]")
+        if wq.numel() < qblk_weight_bytes(wtype, n, k):
+            raise ValueError("wq smaller than the packed size")
+        if xq.numel() < qblk_act_bytes(batch, k):
+            raise ValueError("xq smaller than qblk_act_bytes(batch, k)")
+        descs[i] = GemvDesc(_ptr(wq), int(n), int(k), _ptr(xq), _ptr(y), y.stride(0))
+    _check(_load().qblk_gemv_multi(_type(wtype), ctypes.cast(descs, ctypes.c_void_p), len(products), int(batch),
+                                   _stream(stream)), "qblk_gemv_multi")
+    return [p[4] for p in products]
 
 
 def qblk_gemv_float(wtype, wq, n, k, x, batch=None, y=None, stream=None):

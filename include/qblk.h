@@ -166,6 +166,32 @@ int qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void *xq,
               int64_t batch, float *y, int64_t ldy, hipStream_t stream);
 
 /*
+ * Several independent decode-path products in one launch: a descriptor list
+ * (e.g. the q, k and v projections of a layer kept as separate matrices, all
+ * reading the same or different activations). Each descriptor is one
+ * qblk_gemv with the shared type and batch:
+ *   wq : packed weights [n] rows of k;  xq : activation buffer of `batch`
+ *   rows of k;  y : fp32 [batch][ldy].
+ * The descriptors are read on the host during the call (the array need not
+ * outlive it); their outputs must not overlap. Results are bit-identical to
+ * qblk_gemv on each descriptor. Descriptors with n == 0 are skipped.
+ * Errors: QBLK_ERR_ARG (type, count < 0, null descs), the qblk_gemv errors of
+ * any descriptor, QBLK_ERR_UNSUPPORTED (count > QBLK_GEMV_MULTI_MAX, batch >
+ * QBLK_GEMV_MAX_BATCH).
+ */
+#define QBLK_GEMV_MULTI_MAX 16
+typedef struct qblk_gemv_desc {
+  const void *wq;
+  int64_t n;
+  int64_t k;
+  const void *xq;
+  float *y;
+  int64_t ldy;
+} qblk_gemv_desc;
+int qblk_gemv_multi(int type, const qblk_gemv_desc *descs, int count, int64_t batch,
+                    hipStream_t stream);
+
+/*
  * Decode-path product with the activation quantization fused in: the same
  * result, bit for bit, as qblk_quantize_act(x) followed by qblk_gemv, in one
  * launch. The activation is quantized with the qblk_quantize_act rule

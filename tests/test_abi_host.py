@@ -202,3 +202,25 @@ def test_kv_cache_validation():
     assert sc(2, c, 8, 100, 10, 128, q, 64, _p(FAKE + 2), 10, NULL) == ERR_ALIGN
     assert sc(2, c, 4, 100, 10, 128, q, 64, s, 10, NULL) == ERR_UNSUPPORTED  # group 16
     assert sc(2, NULL, 8, 100, 0, 128, NULL, 64, NULL, 0, NULL) == OK        # no tokens
+
+
+def test_gemv_multi_validation():
+    lib = qblk.lib()
+    f = lib.qblk_gemv_multi
+    D = qblk.GemvDesc
+    good = D(FAKE, 16, 256, FAKE + 0x100000, FAKE + 0x200000, 16)
+    arr = (D * 17)(*([good] * 17))
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    assert f(9, p, 1, 1, NULL) == ERR_ARG                       # unknown type
+    assert f(3, p, -1, 1, NULL) == ERR_ARG                      # negative count
+    assert f(3, NULL, 1, 1, NULL) == ERR_ARG                    # null descriptors
+    assert f(3, NULL, 0, 1, NULL) == OK                         # empty list
+    assert f(3, p, 1, 0, NULL) == OK                            # no activation rows
+    assert f(3, p, 17, 1, NULL) == ERR_UNSUPPORTED              # too many descriptors
+    assert f(3, p, 2, 65, NULL) == ERR_UNSUPPORTED              # batch
+    bad = (D * 2)(good, D(FAKE, 16, 288, FAKE, FAKE, 16))     # Q4_K k % 256 in the second
+    assert f(3, ctypes.cast(bad, ctypes.c_void_p), 2, 1, NULL) == ERR_SHAPE
+    bad = (D * 2)(good, D(FAKE + 8, 16, 256, FAKE, FAKE, 16))
+    assert f(3, ctypes.cast(bad, ctypes.c_void_p), 2, 1, NULL) == ERR_ALIGN
+    bad = (D * 2)(good, D(FAKE, 16, 256, FAKE, FAKE, 15))     # ldy < n
+    assert f(3, ctypes.cast(bad, ctypes.c_void_p), 2, 1, NULL) == ERR_SHAPE

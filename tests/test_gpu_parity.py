@@ -535,3 +535,49 @@ def test_kv_scores_70b_shape_sampled():
     s = host(qblk.qblk_kv_scores(o.TYPE_Q8_0, cache, n_kv, n_ctx, n_ctx, hd, dev_quantize(q), n_head))
     toks = _sample_rows(n_ctx, 200, 151)
     check_rel(s[:, toks], o.kv_scores(o.TYPE_Q8_0, k[:, toks], q, n_head)[1])
+
+
+# ================================================================ multi-product launch
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("batch,ks", [(1, (4096, 4096, 2304)), (3, (1024, 1024, 2048)),
+                                      (1, (28672, 4096, 256)), (9, (512, 512, 768))])
+def test_gemv_multi_matches_single_products(wtype, batch, ks):
+    """Three descriptors (q/k/v-like row counts, one with its own activation
+    and k) in one launch: each output is bit-identical to its own qblk_gemv
+    and within the bar of the oracle."""
+    print(f"gemv multi {TNAME[wtype]} batch={batch} ks={ks}", flush=True)
+    rng = np.random.default_rng(160 + wtype + batch)
+    ns = (300, 77, 1030)
+    prods, refs = [], []
+    xs = {}
+    for n, k in zip(ns, ks):
+        if wtype == o.TYPE_Q4_K and k % 256:
+            k = 256 * max(1, k // 256)
+        w = _special_rows(rng, n, k)
+        if k not in xs:
+            xs[k] = rng.standard_normal((batch, k)).astype(np.float32)
+        wq, xq = dev_pack(wtype, w), dev_quantize(xs[k])
+        y = torch().full((batch, n + 3), -4.0, device="cuda")
+        prods.append((wq, n, k, xq, y[:, :n]))
+        refs.append((w, xs[k], qblk.qblk_gemv(wtype, wq, n, k, xq, batch), y))
+    qblk.qblk_gemv_multi(wtype, prods, batch)
+    for (w, x, ysingle, ybig), (_, n, k, _, _) in zip(refs, prods):
+        yh = host(ybig)
+        assert np.array_equal(yh[:, :n], host(ysingle))
+        assert np.all(yh[:, n:] == -4.0)
+        check_rel(yh[:, :n], expected(wtype, w, x))
+
+
+def test_gemv_multi_skips_empty_descriptors():
+    print("gemv multi empty descriptors", flush=True)
+    rng = np.random.default_rng(170)
+    k = 1024
+    w = _special_rows(rng, 64, k)
+    x = rng.standard_normal((1, k)).astype(np.float32)
+    wq, xq = dev_pack(o.TYPE_Q8_0, w), dev_quantize(x)
+    y = torch().zeros((1, 64), device="cuda")
+    empty = torch().full((1, 1), -3.0, device="cuda")
+    qblk.qblk_gemv_multi(o.TYPE_Q8_0, [(wq, 0, k, xq, empty), (wq, 64, k, xq, y)], 1)
+    check_rel(host(y), expected(o.TYPE_Q8_0, w, x))
+    assert host(empty)[0, 0] == -3.0
