@@ -4,8 +4,9 @@
 // idle and most of each tile empty, while the product is still a stream of
 // the whole weight matrix. This form keeps every weight byte read once and
 // spreads the work over many small workgroups instead:
-//   * a workgroup owns 16 * NT weight rows (columns n of Y) and all m rows of
-//     X, padded to 16 * MT;
+//   * a workgroup owns 16 * NT weight rows (columns n of Y: 64 for m <= 32,
+//     32 for m <= 64, where the registers allow fewer) and all m rows of X,
+//     padded to 16 * MT;
 //   * its four waves split the reduction over k into four contiguous,
 //     super-block-aligned quarters and add their partial tiles in LDS at the
 //     end, in a fixed order (the result does not depend on scheduling);
@@ -49,48 +50,66 @@ constexpr float kMagic = 12582912.0f;
 template <int TYPE>
 constexpr bool kHasMin = TYPE != kQ8_0;
 
-// Wave-private table of decoded weight scales for one 8-block chunk:
-// sw = block scale (Q4_K: d * sc_j), wm = min coefficient (Q4_K: d_min * mn_j;
-// Q4_0: -8 d). Blocks past the wave's range hold zeros.
+// Wave-private table of decoded weight scales for one 8-block chunk of the
+// workgroup's 16 * NT weight rows: sw = block scale (Q4_K: d * sc_j), wm = min
+// coefficient (Q4_K: d_min * mn_j; Q4_0: -8 d). Blocks past the wave's range
+// hold zeros.
+template <int NT>
 struct ScaleTable {
-  float sw[kSb][32];
-  float wm[kSb][32];
+  float sw[kSb][16 * NT];
+  float wm[kSb][16 * NT];
 };
 
 // LDS of a workgroup: the waves' scale tables during the loop, then their
 // partial tiles for the final sum.
 template <int MT, int NT, int WAVES>
 union Shared {
-  ScaleTable tab[WAVES];
+  ScaleTable<NT> tab[WAVES];
   float red[WAVES][MT][NT][4][64];
 };
 
-// Raw scale data of one chunk for one lane: Q4_K = the super-block header of
-// weight row (lane & 31); other types = four block scales (fp32, or fp16 for
-// Q4_0_F16) of blocks [c0 + 4 h, c0 + 4 h + 4), h = lane >> 5.
+// The table of a chunk is filled by all 64 lanes: lane = (column c, part h)
+// with c = lane % (16 NT) and P = 64 / (16 NT) parts per column. Raw data of
+// one lane: Q4_K = the column's super-block header (part h decodes values
+// [16h/P, 16(h+1)/P) of its 8 scale and 8 min codes); other types = the block
+// scales (fp32, or fp16 for Q4_0_F16) of blocks [c0 + h 8/P, c0 + (h+1) 8/P).
 struct RawScales {
-  uint4 v;
+  uint4 v[2];
 };
+
+template <int NT>
+constexpr int kParts = 64 / (16 * NT);
 
 template <int TYPE, int NT>
 __device__ __forceinline__ RawScales load_scales(const WeightView& W, int64_t n0, int64_t n, int64_t nb,
                                                  int64_t c0, int lane) {
+  constexpr int P = kParts<NT>;
+  constexpr int kBlk = kSb / P;  // blocks per part (non-K types)
   RawScales r;
-  r.v = make_uint4(0, 0, 0, 0);
-  const int col = lane & 31;
-  if (col >= 16 * NT) return r;
+  r.v[0] = r.v[1] = make_uint4(0, 0, 0, 0);
+  const int col = lane % (16 * NT);
+  const int h = lane / (16 * NT);
   const int64_t gn = n0 + col < n ? n0 + col : n - 1;
   const uint8_t* row = W.row(gn);
   if constexpr (TYPE == kQ4_K) {
-    r.v = load16(row + 16 * (c0 / kSb));
+    r.v[0] = load16(row + 16 * (c0 / kSb));
   } else {
-    const int64_t b = c0 + 4 * (lane >> 5);
-    if (b < nb) {  // the padded header keeps the 4-block read in bounds
-      if constexpr (TYPE == kQ4_0H) {
-        const uint2 h = *reinterpret_cast<const uint2*>(row + 2 * b);
-        r.v = make_uint4(h.x, h.y, 0, 0);
-      } else {
-        r.v = load16(row + 4 * b);
+    const int64_t b = c0 + kBlk * h;
+    // reads stay inside the zero-padded header: b and b + 4 are multiples of
+    // 4 blocks, each read only when its first block exists
+    if constexpr (TYPE == kQ4_0H) {
+      if (b < nb) {
+        if constexpr (kBlk == 8) r.v[0] = load16(row + 2 * b);
+        else if constexpr (kBlk == 4) { const uint2 x = *reinterpret_cast<const uint2*>(row + 2 * b); r.v[0] = make_uint4(x.x, x.y, 0, 0); }
+        else r.v[0].x = *reinterpret_cast<const uint32_t*>(row + 2 * b);
+      }
+    } else {
+      if (b < nb) {
+        if constexpr (kBlk >= 4) r.v[0] = load16(row + 4 * b);
+        else { const uint2 x = *reinterpret_cast<const uint2*>(row + 4 * b); r.v[0] = make_uint4(x.x, x.y, 0, 0); }
+      }
+      if constexpr (kBlk == 8) {
+        if (b + 4 < nb) r.v[1] = load16(row + 4 * (b + 4));
       }
     }
   }
@@ -108,40 +127,46 @@ __device__ __forceinline__ uint32_t field6(const uint4& h, int b) {
 
 // Decode one chunk into the table; blocks at or past `jend` get zeros.
 template <int TYPE, int NT>
-__device__ __forceinline__ void decode_scales(ScaleTable* __restrict__ t, const RawScales& r, int64_t c0,
+__device__ __forceinline__ void decode_scales(ScaleTable<NT>* __restrict__ t, const RawScales& r, int64_t c0,
                                               int64_t jend, int lane) {
-  const int col = lane & 31;
-  const int h = lane >> 5;
-  if (col >= 16 * NT) return;
+  constexpr int P = kParts<NT>;
+  const int col = lane % (16 * NT);
+  const int h = lane / (16 * NT);
   if constexpr (TYPE == kQ4_K) {
     // jend is a multiple of 8 here (k is a multiple of 256): the chunk is whole
-    if (h == 0) {
-      const float d = half_bits_to_float(r.v.x);
+    constexpr int kVals = 16 / P;
+    const float d = half_bits_to_float(r.v[0].x);
+    const float dmin = half_bits_to_float(r.v[0].x >> 16);
 #pragma unroll
-      for (int j = 0; j < kSb; ++j) t->sw[j][col] = d * static_cast<float>(field6(r.v, 6 * j));  // sc_j
-    } else {
-      const float dmin = half_bits_to_float(r.v.x >> 16);
+    for (int pp = 0; pp < P; ++pp) {
+      if (h == pp) {  // the part index is a compile-time constant inside
 #pragma unroll
-      for (int j = 0; j < kSb; ++j) t->wm[j][col] = dmin * static_cast<float>(field6(r.v, 48 + 6 * j));  // mn_j
+        for (int i = 0; i < kVals; ++i) {
+          const int v = pp * kVals + i;
+          if (v < 8) t->sw[v][col] = d * static_cast<float>(field6(r.v[0], 6 * v));              // sc_v
+          else t->wm[v - 8][col] = dmin * static_cast<float>(field6(r.v[0], 48 + 6 * (v - 8)));  // mn_(v-8)
+        }
+      }
     }
   } else {
-    float d[4];
-    if constexpr (TYPE == kQ4_0H) {
-      d[0] = half_bits_to_float(r.v.x);
-      d[1] = half_bits_to_float(r.v.x >> 16);
-      d[2] = half_bits_to_float(r.v.y);
-      d[3] = half_bits_to_float(r.v.y >> 16);
-    } else {
-      d[0] = __uint_as_float(r.v.x);
-      d[1] = __uint_as_float(r.v.y);
-      d[2] = __uint_as_float(r.v.z);
-      d[3] = __uint_as_float(r.v.w);
+    constexpr int kBlk = kSb / P;
+    float d[kBlk];
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i) {
+      if constexpr (TYPE == kQ4_0H) {
+        const uint32_t w = i < 2 ? r.v[0].x : i < 4 ? r.v[0].y : i < 6 ? r.v[0].z : r.v[0].w;
+        d[i] = half_bits_to_float(w >> (16 * (i & 1)));
+      } else {
+        const uint4& v = r.v[i / 4];
+        const int e = i % 4;
+        d[i] = __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = c0 + 4 * h + i < jend;
-      t->sw[4 * h + i][col] = ok ? d[i] : 0.0f;
-      if constexpr (kHasMin<TYPE>) t->wm[4 * h + i][col] = ok ? -8.0f * d[i] : 0.0f;  // nibble - 8
+    for (int i = 0; i < kBlk; ++i) {
+      const bool ok = c0 + kBlk * h + i < jend;
+      t->sw[kBlk * h + i][col] = ok ? d[i] : 0.0f;
+      if constexpr (kHasMin<TYPE>) t->wm[kBlk * h + i][col] = ok ? -8.0f * d[i] : 0.0f;  // nibble - 8
     }
   }
 }
@@ -186,7 +211,7 @@ struct Sources {
   __amdgpu_buffer_rsrc_t w;    // this workgroup's weight rows
   __amdgpu_buffer_rsrc_t a;    // activation codes [m][k]
   __amdgpu_buffer_rsrc_t ds;   // activation (d, code sum) pairs [m][nb]
-  uint32_t w_off[2];           // byte offset of block q of weight row 16 nt + r
+  uint32_t w_off[4];           // byte offset of block q of weight row 16 nt + r
   uint32_t a_off[4];           // byte offset of block q of activation row 16 mt + r
   uint32_t ds_off[4];          // byte offset of block q's pair of activation row 16 mt + r
 };
@@ -229,7 +254,7 @@ __device__ __forceinline__ long pack64(uint32_t lo, uint32_t hi) {
 }
 
 template <int TYPE, int MT, int NT>
-__device__ __forceinline__ void compute_group(Ops<TYPE, MT, NT> o, const ScaleTable* __restrict__ t, int jt,
+__device__ __forceinline__ void compute_group(Ops<TYPE, MT, NT> o, const ScaleTable<NT>* __restrict__ t, int jt,
                                               int64_t j0, int64_t jend, int q, int r, v4f (&acc)[MT][NT]) {
   // exchange: afterwards the 4-bit weights' w[nt][jj], the 8-bit weights'
   // (w[nt][2 jj], w[nt][2 jj + 1]) and the activations' (a[mt][2 jj],
@@ -311,7 +336,7 @@ __device__ __forceinline__ void compute_group(Ops<TYPE, MT, NT> o, const ScaleTa
 template <int TYPE, int MT, int NT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(WeightView W, int64_t n, int64_t nb, ActView A,
                                                                 int64_t m, float* __restrict__ y, int64_t ldy) {
-  static_assert(MT <= 4 && NT <= 2, "operand offsets are sized for 4 x 2 tiles");
+  static_assert(MT <= 4 && NT <= 4, "operand offsets are sized for 4 x 4 tiles");
   __shared__ __attribute__((aligned(16))) Shared<MT, NT, WAVES> sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -349,7 +374,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(WeightView W, in
       src.a_off[mt] = static_cast<uint32_t>((16 * mt + r) * A.k) + 32u * q;
       src.ds_off[mt] = static_cast<uint32_t>((16 * mt + r) * nb * 8) + 8u * q;
     }
-    ScaleTable* tab = &sh.tab[wave];
+    ScaleTable<NT>* tab = &sh.tab[wave];
 
     // two operand sets in turn: group 0 of a chunk computes from `ga` while
     // group 1's operands stream into `gb`, then the roles swap (no register
@@ -410,8 +435,8 @@ void launch_t(const WeightView& W, int64_t n, int64_t nb, const ActView& A, int6
 template <int TYPE>
 void launch_type(const WeightView& W, int64_t n, int64_t nb, const ActView& A, int64_t m, float* y,
                  int64_t ldy, hipStream_t s) {
-  if (m <= 16) launch_t<TYPE, 1, 2, kWaves>(W, n, nb, A, m, y, ldy, s);
-  else if (m <= 32) launch_t<TYPE, 2, 2, kWaves>(W, n, nb, A, m, y, ldy, s);
+  if (m <= 16) launch_t<TYPE, 1, 4, kWaves>(W, n, nb, A, m, y, ldy, s);
+  else if (m <= 32) launch_t<TYPE, 2, 4, kWaves>(W, n, nb, A, m, y, ldy, s);
   else launch_t<TYPE, 4, 2, kWaves>(W, n, nb, A, m, y, ldy, s);
 }
 
