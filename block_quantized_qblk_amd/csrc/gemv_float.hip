@@ -184,10 +184,12 @@ void launch_rb(const WeightView& W, int64_t n, int64_t nb, const float* x, int64
 template <int TYPE>
 void launch_t(const WeightView& W, int64_t n, int64_t nb, const float* x, int64_t ldx, int batch, float* y,
               int64_t ldy, hipStream_t s) {
-  if (batch == 1) launch_rb<TYPE, 2, 1>(W, n, nb, x, ldx, batch, y, ldy, s);
-  else if (batch == 2) launch_rb<TYPE, 2, 2>(W, n, nb, x, ldx, batch, y, ldy, s);
-  else if (batch <= 4) launch_rb<TYPE, 2, 4>(W, n, nb, x, ldx, batch, y, ldy, s);
-  else launch_rb<TYPE, 1, 8>(W, n, nb, x, ldx, batch, y, ldy, s);
+  // 4 rows per wave share each activation read (measured on MI355X: 1.2-1.5x
+  // faster than 2 at batch 1 and 4; 8 is no better)
+  if (batch == 1) launch_rb<TYPE, 4, 1>(W, n, nb, x, ldx, batch, y, ldy, s);
+  else if (batch == 2) launch_rb<TYPE, 4, 2>(W, n, nb, x, ldx, batch, y, ldy, s);
+  else if (batch <= 4) launch_rb<TYPE, 4, 4>(W, n, nb, x, ldx, batch, y, ldy, s);
+  else launch_rb<TYPE, 2, 8>(W, n, nb, x, ldx, batch, y, ldy, s);
 }
 
 }  // namespace
