@@ -374,8 +374,9 @@ def traffic_from_profile(path, sources):
 def traffic_probe(torch, qblk, synth, dev):
     """For rocprofv3 --pmc runs: a 1 GiB device copy (calibration), one decode
     token of four 70B-shaped layers at batch 1 (per layer: qkv, o, gate_up,
-    down), then one Q4_K GEMM of 512 x 14336 x 4096. Prints the algorithmic
-    bytes of every GEMV and GEMM launch, in launch order."""
+    down), then one Q4_K GEMM of 512 x 14336 x 4096 and one of 64 x 14336 x
+    4096. Prints the algorithmic bytes of every GEMV launch and of the 512-row
+    GEMM, in launch order."""
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -398,6 +399,11 @@ def traffic_probe(torch, qblk, synth, dev):
     torch.cuda.synchronize()
     gemm = {"m": mm, "n": n, "k": k, "alg_bytes": qblk.qblk_weight_bytes(qblk.Q4_K, n, k)
             + qblk.qblk_act_bytes(mm, k) + 4 * mm * n}
+    # the few-rows form on the same weights (m = 64)
+    ms = 64
+    xs = qblk.qblk_quantize_act(synth.torch_activations(4098, ms, k, device=dev))
+    qblk.qblk_gemm(qblk.Q4_K, wq, n, k, xs, ms, y=y[:ms])
+    torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_each_way": 1 << 30, "gemv_launches": gemv,
                       "gemm_launch": gemm,
                       "gemv_sources_sha256": sources_sha256(GEMV_SOURCES),
