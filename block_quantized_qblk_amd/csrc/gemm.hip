@@ -48,7 +48,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int BM = 128;        // activation rows per workgroup
 constexpr int BN = 128;        // weight rows per workgroup
 constexpr int KB = 4;          // 32-blocks per K step
-constexpr int kThreads = 256;  // 4 waves, 2 x 2, each 64 x 64
+// waves per workgroup: kWaves / kWavesN along M, kWavesN along N (measured
+// on MI355X: 8 waves of 32 x 64 are 2-4% faster for Q4_0 / Q8_0 but 13% slower
+// for Q4_K, whose scale step needs more registers)
+constexpr int kWaves = 4;
+constexpr int kWavesN = 2;
+constexpr int TM = BM / 32 / (kWaves / kWavesN);  // 32-row MFMA tiles per wave
+constexpr int TN = BN / 32 / kWavesN;             // 32-column MFMA tiles per wave
+constexpr int kThreads = 64 * kWaves;
+constexpr int kAInstr = BM * 8 / 64 / kWaves;     // activation DMA instructions per wave and stage
 constexpr int kMagicBits = 0x4B400000;  // fp32 1.5 * 2^23
 constexpr float kMagic = 12582912.0f;
 
@@ -107,12 +115,12 @@ struct GemmCtx {
 template <int TYPE>
 struct DmaLanes {
   static constexpr int kUnits = Cfg<TYPE>::kWRow / 16;  // weight units per row
-  static constexpr int kInstr = BN * kUnits / 64 / 4;   // weight loads per wave
+  static constexpr int kInstr = BN * kUnits / 64 / kWaves;  // weight loads per wave
   const uint8_t* a_base;
   const uint8_t* w_base;
-  uint32_t a_off[4];
+  uint32_t a_off[kAInstr];
   uint32_t w_off[kInstr];
-  int a_unit[4];
+  int a_unit[kAInstr];
   int w_unit[kInstr];
 };
 
@@ -123,8 +131,8 @@ __device__ __forceinline__ DmaLanes<TYPE> dma_lanes(const GemmCtx<TYPE>& g, int 
   d.a_base = g.A.q + g.m0 * k;
   d.w_base = g.W.base + g.n0 * g.W.row_bytes + g.W.hdr_bytes;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = 64 * (4 * wave + i) + lane;  // unit index in the stage
+  for (int i = 0; i < kAInstr; ++i) {
+    const int u = 64 * (kAInstr * wave + i) + lane;  // unit index in the stage
     const int r = u >> 3;
     d.a_unit[i] = a_pos(r, u & 7);  // global unit stored at this position
     const int64_t rr = g.m0 + r < g.m ? r : g.m - 1 - g.m0;
@@ -150,10 +158,11 @@ __device__ __forceinline__ void issue_codes(const GemmCtx<TYPE>& g, const DmaLan
   const int nblk = static_cast<int>(g.nb - blk0 < KB ? g.nb - blk0 : KB);
   const uint32_t a_step = static_cast<uint32_t>(32 * blk0);
   const uint32_t w_step = static_cast<uint32_t>((Cfg<TYPE>::kWRow / KB) * blk0);
-  // activations: BM rows x 8 units = 16 instructions, 4 per wave
+  // activations: BM rows x 8 units = 16 instructions, kAInstr per wave
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (d.a_unit[i] < 2 * nblk) lds_dma16(d.a_base + (d.a_off[i] + a_step), S->a + 1024 * (4 * wave + i));
+  for (int i = 0; i < kAInstr; ++i) {
+    if (d.a_unit[i] < 2 * nblk)
+      lds_dma16(d.a_base + (d.a_off[i] + a_step), S->a + 1024 * (kAInstr * wave + i));
   }
   // weights
   constexpr int kPerBlk = DmaLanes<TYPE>::kUnits / KB;  // units per block (1 or 2)
@@ -171,9 +180,12 @@ struct ScaleRegs {
   uint4 wgt;  // Q4_K header / four fp32 block scales of one weight row
 };
 
-// Per-thread scale sources, fixed for the launch: the (d, sum) pairs of
-// blocks 2h, 2h+1 of activation row tid/2, and weight row tid's header /
-// scale region (threads below BN).
+// Per-thread scale sources, fixed for the launch: threads below 2 BM load
+// the (d, sum) pairs of blocks 2h, 2h+1 of activation row tid/2; threads
+// kWgtBase + i (i < BN) the header / scale region of weight row i.
+constexpr int kWgtBase = kThreads >= 2 * BM + BN ? 2 * BM : 0;
+__device__ __forceinline__ bool act_lane(int tid) { return tid < 2 * BM; }
+__device__ __forceinline__ int wgt_row(int tid) { return tid - kWgtBase; }  // valid in [0, BN)
 struct ScaleLanes {
   const uint8_t* act;
   const uint8_t* wgt;
@@ -182,10 +194,11 @@ struct ScaleLanes {
 template <int TYPE>
 __device__ __forceinline__ ScaleLanes scale_lanes(const GemmCtx<TYPE>& g, int tid) {
   ScaleLanes l;
-  const int r = tid >> 1, h = tid & 1;
+  const int r = (tid >> 1) & (BM - 1), h = tid & 1;
   const int64_t gm = g.m0 + r < g.m ? g.m0 + r : g.m - 1;
   l.act = g.A.ds + 8 * (gm * g.nb + 2 * h);
-  const int64_t gn = g.n0 + (tid & (BN - 1)) < g.n ? g.n0 + (tid & (BN - 1)) : g.n - 1;
+  const int wr = wgt_row(tid) & (BN - 1);
+  const int64_t gn = g.n0 + wr < g.n ? g.n0 + wr : g.n - 1;
   l.wgt = g.W.row(gn);
   return l;
 }
@@ -201,11 +214,11 @@ __device__ __forceinline__ ScaleRegs load_scales(const GemmCtx<TYPE>& g, const S
   // second block may lie past the last block of the row
   const uint8_t* src = sl.act + 8 * blk0;
   uint2 p0 = make_uint2(0, 0), p1 = make_uint2(0, 0);
-  if (2 * h < nblk) p0 = *reinterpret_cast<const uint2*>(src);
-  if (2 * h + 1 < nblk) p1 = *reinterpret_cast<const uint2*>(src + 8);
+  if (act_lane(tid) && 2 * h < nblk) p0 = *reinterpret_cast<const uint2*>(src);
+  if (act_lane(tid) && 2 * h + 1 < nblk) p1 = *reinterpret_cast<const uint2*>(src + 8);
   s.act = make_uint4(p0.x, p0.y, p1.x, p1.y);
   s.wgt = make_uint4(0, 0, 0, 0);
-  if (tid < BN) {
+  if (wgt_row(tid) >= 0 && wgt_row(tid) < BN) {
     if constexpr (TYPE == kQ4_K) {
       s.wgt = load16(sl.wgt + 16 * (blk0 >> 3));
     } else if constexpr (TYPE == kQ4_0H) {
@@ -226,21 +239,24 @@ __device__ __forceinline__ void store_scales(Stage<TYPE>* __restrict__ S, const 
   const int r = tid >> 1;
   const int h = tid & 1;
   const float d0 = __uint_as_float(s.act.x), d1 = __uint_as_float(s.act.z);
-  S->sa[2 * h][r] = d0;
-  S->sa[2 * h + 1][r] = d1;
-  if constexpr (Cfg<TYPE>::kHasMin) {
-    S->mn.asc[2 * h][r] = d0 * static_cast<float>(static_cast<int>(s.act.y));
-    S->mn.asc[2 * h + 1][r] = d1 * static_cast<float>(static_cast<int>(s.act.w));
+  if (act_lane(tid)) {
+    S->sa[2 * h][r] = d0;
+    S->sa[2 * h + 1][r] = d1;
+    if constexpr (Cfg<TYPE>::kHasMin) {
+      S->mn.asc[2 * h][r] = d0 * static_cast<float>(static_cast<int>(s.act.y));
+      S->mn.asc[2 * h + 1][r] = d1 * static_cast<float>(static_cast<int>(s.act.w));
+    }
   }
-  if (tid < BN) {
+  const int wr = wgt_row(tid);
+  if (wr >= 0 && wr < BN) {
     if constexpr (TYPE == kQ4_K) {
       const float d = half_bits_to_float(s.wgt.x);
       const float dmin = half_bits_to_float(s.wgt.x >> 16);
       const int j0 = static_cast<int>((st * KB) & 7);
 #pragma unroll
       for (int jj = 0; jj < KB; ++jj) {
-        S->sw[jj][tid] = d * static_cast<float>(q4k_sc(s.wgt, j0 + jj));
-        S->mn.wm[jj][tid] = dmin * static_cast<float>(q4k_mn(s.wgt, j0 + jj));
+        S->sw[jj][wr] = d * static_cast<float>(q4k_sc(s.wgt, j0 + jj));
+        S->mn.wm[jj][wr] = dmin * static_cast<float>(q4k_mn(s.wgt, j0 + jj));
       }
     } else {
       float dw[4] = {__uint_as_float(s.wgt.x), __uint_as_float(s.wgt.y),
@@ -253,15 +269,15 @@ __device__ __forceinline__ void store_scales(Stage<TYPE>* __restrict__ S, const 
       }
 #pragma unroll
       for (int jj = 0; jj < KB; ++jj) {
-        S->sw[jj][tid] = dw[jj];
-        if constexpr (Cfg<TYPE>::kHasMin) S->mn.wm[jj][tid] = -8.0f * dw[jj];  // Q4_0: nibble - 8
+        S->sw[jj][wr] = dw[jj];
+        if constexpr (Cfg<TYPE>::kHasMin) S->mn.wm[jj][wr] = -8.0f * dw[jj];  // Q4_0: nibble - 8
       }
     }
   }
 }
 
 struct Acc {
-  v16f main[2][2];  // scale steps (VALU) and min terms (matrix core) accumulate here
+  v16f main[TM][TN];  // scale steps (VALU) and min terms (matrix core) accumulate here
 };
 
 // The MFMAs and scale steps of one K step from stage S.
@@ -269,10 +285,10 @@ template <int TYPE>
 __device__ __forceinline__ void compute(const Stage<TYPE>* __restrict__ S, int nblk, int wm0, int wn0, int half,
                                         int l32, const v16i& cinit, Acc& acc) {
   for (int j = 0; j < nblk; ++j) {
-    v4i bop[2];
-    float sw[2], ncs[2];
+    v4i bop[TN];
+    float sw[TN], ncs[TN];
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
+    for (int tn = 0; tn < TN; ++tn) {
       const int r = wn0 + 32 * tn + l32;
       if constexpr (TYPE == kQ8_0) {
         const uint4 w = *reinterpret_cast<const uint4*>(
@@ -290,7 +306,7 @@ __device__ __forceinline__ void compute(const Stage<TYPE>* __restrict__ S, int n
       ncs[tn] = -kMagic * sw[tn];
     }
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
+    for (int tm = 0; tm < TM; ++tm) {
       const int ra = wm0 + 32 * tm + l32;
       const uint4 a = *reinterpret_cast<const uint4*>(S->a + 128 * ra + 16 * a_pos(ra, 2 * j + half));
       const v4i aop = v4i{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z),
@@ -307,7 +323,7 @@ __device__ __forceinline__ void compute(const Stage<TYPE>* __restrict__ S, int n
         sa[4 * q + 3] = s4.w;
       }
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
+      for (int tn = 0; tn < TN; ++tn) {
         const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop[tn], cinit, 0, 0, 0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -329,15 +345,15 @@ __device__ __forceinline__ void compute(const Stage<TYPE>* __restrict__ S, int n
       if (2 * i < nblk) {  // uniform
         const int b = 2 * i + half;
         const bool okb = b < nblk;
-        float af[2], bf[2];
+        float af[TM], bf[TN];
 #pragma unroll
-        for (int tm = 0; tm < 2; ++tm) af[tm] = okb ? S->mn.asc[b][wm0 + 32 * tm + l32] : 0.0f;
+        for (int tm = 0; tm < TM; ++tm) af[tm] = okb ? S->mn.asc[b][wm0 + 32 * tm + l32] : 0.0f;
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) bf[tn] = okb ? S->mn.wm[b][wn0 + 32 * tn + l32] : 0.0f;
+        for (int tn = 0; tn < TN; ++tn) bf[tn] = okb ? S->mn.wm[b][wn0 + 32 * tn + l32] : 0.0f;
 #pragma unroll
-        for (int tm = 0; tm < 2; ++tm)
+        for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-          for (int tn = 0; tn < 2; ++tn)
+          for (int tn = 0; tn < TN; ++tn)
             acc.main[tm][tn] =
                 __builtin_amdgcn_mfma_f32_32x32x2f32(af[tm], bf[tn], acc.main[tm][tn], 0, 0, 0);
       }
@@ -385,8 +401,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave >> 1) * 64;  // wave's row offset in the tile
-  const int wn0 = (wave & 1) * 64;   // wave's column offset in the tile
+  const int wm0 = (wave / kWavesN) * (32 * TM);  // wave's row offset in the tile
+  const int wn0 = (wave % kWavesN) * (32 * TN);  // wave's column offset in the tile
   const int half = lane >> 5;        // which 16 elements of a block this lane holds
   const int l32 = lane & 31;
 
@@ -401,9 +417,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n,
 
   Acc acc;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < TN; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc.main[a][b][v] = 0.0f;
   v16i cinit;
@@ -427,9 +443,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n,
 
   // ---- store: lane holds column n = l32 and 16 rows of each 32 x 32 tile
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
+    for (int tn = 0; tn < TN; ++tn) {
       const int64_t gn = g.n0 + wn0 + 32 * tn + l32;
       if (gn >= n) continue;
 #pragma unroll
