@@ -48,11 +48,13 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int BM = 128;        // activation rows per workgroup
 constexpr int BN = 128;        // weight rows per workgroup
 constexpr int KB = 4;          // 32-blocks per K step
-// waves per workgroup: kWaves / kWavesN along M, kWavesN along N (measured
-// on MI355X: 8 waves of 32 x 64 are 2-4% faster for Q4_0 / Q8_0 but 13% slower
-// for Q4_K, whose scale step needs more registers)
+// waves per workgroup: kWaves / kWavesN along M, kWavesN along N. Measured
+// on MI355X (512 x 14336 x 4096): 4 waves of 32 x 128 are 4% faster than 2 x 2
+// waves of 64 x 64 for Q4_K (half the activation-scale LDS reads per block)
+// and 2% for Q8_0, 4% slower for Q4_0; 8 waves of 32 x 64 are 13% slower for
+// Q4_K, whose scale step needs more registers.
 constexpr int kWaves = 4;
-constexpr int kWavesN = 2;
+constexpr int kWavesN = 1;
 constexpr int TM = BM / 32 / (kWaves / kWavesN);  // 32-row MFMA tiles per wave
 constexpr int TN = BN / 32 / kWavesN;             // 32-column MFMA tiles per wave
 constexpr int kThreads = 64 * kWaves;
