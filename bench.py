@@ -17,9 +17,11 @@ fraction (HIP-event-timed graphs of back-to-back GEMV launches, the same
 boundary-to-boundary time a kernel trace reports), a 7B-shaped layer with rotated
 weight copies, the prefill GEMM (512 x 14336 x 4096, int8 TOPS) with the
 decode/prefill crossover at M in {1, 8, 64}, the Q4_0 and Q8_0 GEMVs, and the
-CPU oracle on a bounded sample of the same workload.
+CPU oracle on a bounded sample of the same workload (one process per host
+core, and one process alone).
 
     python bench.py [--steps K] [--warmup W] [--layers L] [--no-cpu-baseline]
+                    [--oracle-workers P]
 """
 
 import argparse
@@ -48,6 +50,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--oracle-workers", type=int, default=0,
+                   help="processes for the parallel CPU oracle run (0: one per host core, "
+                        "at most 16; 1: single-process run only)")
     p.add_argument("--traffic-probe", action="store_true",
                    help="only run a 1 GiB device copy and the GEMVs of 4 layers once "
                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
@@ -72,6 +77,19 @@ def device_sleep(torch, seconds):
         torch.cuda.synchronize()
         _SLEEP_CYCLES_PER_S = 10_000_000 / (a.elapsed_time(b) * 1e-3)
     torch.cuda._sleep(int(seconds * _SLEEP_CYCLES_PER_S))
+
+
+def replay_percentiles(torch, graph, n):
+    """p10 / p50 / p90 of `n` single replays, each between two events."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record()
+    for i in range(n):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    t = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+    q = lambda f: t[min(n - 1, int(round(f * (n - 1))))]
+    return {"p10": round(q(0.1), 6), "p50": round(q(0.5), 6), "p90": round(q(0.9), 6), "replays": n}
 
 
 def time_replays(torch, graphs, steps, warmup):
@@ -226,6 +244,11 @@ def main():
                                    "shards by weight rows across GPUs (see the design notes)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    # the parallel oracle run starts its worker processes before anything in
+    # this process touches the GPU
+    cpu_par = None
+    if not args.no_cpu_baseline and not args.traffic_probe:
+        cpu_par = cpu_baseline_parallel(args.cpu_seconds, args.oracle_workers)
     import torch
     from block_quantized_qblk_amd import qblk, synth
 
@@ -245,6 +268,8 @@ def main():
     value = m1.weight_bytes / (ms_tok * 1e-3) / 1e9
     log(f"batch 1: {ms_tok:.3f} ms/token, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% "
         f"of HBM peak)")
+    pct_tok = replay_percentiles(torch, g1, max(20, args.steps))
+    log(f"batch 1, single tokens: {pct_tok}")
     del g1
     tot_b, tot_s, per_group = m1.kernel_times(m1.layers)
     all_gemv = tot_b / tot_s / 1e9
@@ -283,6 +308,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(synth, args.cpu_seconds)
+        if cpu_par is not None:
+            single = dict(cpu)
+            single.pop("host_cores", None)
+            cpu = dict(cpu_par, single_process=single)
 
     out = {
         "metric": "Q4_K GEMV effective weight GB/s (% HBM peak); prefill GEMM int8 TOPS",
@@ -304,6 +333,7 @@ def main():
             "weight_bytes_per_step": m_bytes(qblk, synth, args.layers),
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "tokens_per_s": round(1e3 / ms_tok, 2),
+            "ms_per_token_single_replays": pct_tok,
             "batch4_ms_per_step": round(ms_tok4, 6),
             "batch4_GBps": round(m_bytes(qblk, synth, args.layers) / (ms_tok4 * 1e-3) / 1e9, 2),
             "launches_per_token": 4 * args.layers,
@@ -609,15 +639,7 @@ def cpu_baseline(synth, seconds):
     over a bounded sample of the headline workload: the first 32 rows of each
     of the seven 70B-shaped Q4_K linears (encoded untimed), then activation
     quantization plus the product timed, repeated until `seconds` elapse."""
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    from oracle import qblk_oracle as o
-    rows = 32
-    samples = []
-    for idx, (name, n, k) in enumerate(synth.LAYER_70B):
-        w = synth.weights_student_t(5900 + idx, rows, k)
-        _, enc = o.encode_weights(o.TYPE_Q4_K, w)
-        x = synth.activations(5999 - idx, 1, k)
-        samples.append((enc, x, o.row_bytes(o.TYPE_Q4_K, k) * rows))
+    o, samples, rows = _oracle_samples(synth)
     done_bytes = 0
     t0 = time.perf_counter()
     reps = 0
@@ -638,6 +660,73 @@ def cpu_baseline(synth, seconds):
                       f"block sums + fp64 scaling; weight encoding untimed); NumPy's int64 "
                       f"einsum runs on one thread",
             "host_cores": len(os.sched_getaffinity(0))}
+
+
+def _oracle_samples(synth):
+    """The first 32 rows of each of the seven 70B-shaped Q4_K linears, encoded
+    by the oracle, with one activation row each."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import qblk_oracle as o
+    rows = 32
+    samples = []
+    for idx, (name, n, k) in enumerate(synth.LAYER_70B):
+        w = synth.weights_student_t(5900 + idx, rows, k)
+        _, enc = o.encode_weights(o.TYPE_Q4_K, w)
+        x = synth.activations(5999 - idx, 1, k)
+        samples.append((enc, x, o.row_bytes(o.TYPE_Q4_K, k) * rows))
+    return o, samples, rows
+
+
+def _oracle_worker(barrier, results, seconds):
+    from block_quantized_qblk_amd import synth
+    o, samples, _ = _oracle_samples(synth)
+    barrier.wait()
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for enc, x, nbytes in samples:
+            o.product(o.TYPE_Q4_K, enc, o.quantize_act(x))
+            done += nbytes
+    results.put((done, time.perf_counter() - t0))
+
+
+def cpu_baseline_parallel(seconds, workers):
+    """The oracle on every host core at once: `workers` single-threaded
+    processes, each running the cpu_baseline sample loop for `seconds` after a
+    common start barrier; throughput is their total bytes over the mean
+    elapsed time."""
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    w = workers if workers > 0 else min(16, cores)
+    if w <= 1:
+        return None
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in env:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        barrier, results = ctx.Barrier(w), ctx.Queue()
+        procs = [ctx.Process(target=_oracle_worker, args=(barrier, results, seconds)) for _ in range(w)]
+        for p in procs:
+            p.start()
+        got = [results.get(timeout=seconds + 300) for _ in range(w)]
+        for p in procs:
+            p.join(timeout=60)
+    finally:
+        for k, v in env.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    total = sum(b for b, _ in got)
+    el = sum(e for _, e in got) / len(got)
+    gbs = total / el / 1e9
+    log(f"cpu oracle, {w} processes: {gbs:.4f} GB/s over {el:.1f}s")
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": w, "kind": "oracle",
+            "sample": f"{w} single-threaded processes, each repeating the single-process sample "
+                      f"(first 32 rows of each of the 7 Q4_K linears of a 70B-shaped layer, batch 1: "
+                      f"activation quantization + int64 block sums + fp64 scaling) for {el:.1f}s "
+                      f"after a common start",
+            "host_cores": cores}
 
 
 if __name__ == "__main__":
