@@ -717,7 +717,10 @@ def cpu_baseline_parallel(seconds, workers):
     import multiprocessing as mp
     cores = len(os.sched_getaffinity(0))
     w = workers if workers > 0 else min(16, cores)
-    if w <= 1:
+    # under a profiler (rocprofv3 preloads its tool into every child) the
+    # workers would each carry the tool; leave the parallel run out there
+    profiled = any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", "")
+    if w <= 1 or profiled:
         return None
     env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in env:
