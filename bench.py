@@ -61,24 +61,6 @@ def parse():
 
 # ---------------------------------------------------------------- timing helpers
 
-_SLEEP_CYCLES_PER_S = None
-
-
-def device_sleep(torch, seconds):
-    """Keep the GPU busy for about `seconds` so that work queued meanwhile
-    runs back to back (host launch latency stays outside event brackets)."""
-    global _SLEEP_CYCLES_PER_S
-    if _SLEEP_CYCLES_PER_S is None:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(1000)
-        a.record()
-        torch.cuda._sleep(10_000_000)
-        b.record()
-        torch.cuda.synchronize()
-        _SLEEP_CYCLES_PER_S = 10_000_000 / (a.elapsed_time(b) * 1e-3)
-    torch.cuda._sleep(int(seconds * _SLEEP_CYCLES_PER_S))
-
-
 def replay_percentiles(torch, graph, n):
     """p10 / p50 / p90 of `n` single replays, each between two events."""
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
@@ -463,36 +445,32 @@ def layer_7b(torch, qblk, synth, dev, args):
     return res
 
 
-def timed_launches(torch, fn, iters, warm_s=0.0):
-    """Mean duration of `iters` launches of fn(i), each between two events.
-
-    With `warm_s` > 0 the timed launches follow about `warm_s` seconds of
-    untimed launches back to back, with no host wait in between: on MI355X a
+def graph_launches(torch, fn, launches=64, reps=5, warm_s=0.0):
+    """Mean per-launch time (us) of fn(0..launches-1) captured back to back
+    in one HIP graph and replayed `reps` times between two events on the
+    launch stream: the boundary-to-boundary duration a kernel trace reports,
+    without per-launch event packets. The timed replays follow about
+    `warm_s` seconds of untimed ones (at least one): on MI355X a
     compute-bound kernel runs about 20% slower during its first ~30 ms of
-    sustained load (and again after an idle gap) while the engine clock
-    settles. Otherwise a sleep kernel queues the timed launches so that host
-    launch latency stays outside the event brackets."""
-    for _ in range(3):
-        fn(0)
+    sustained load, as the engine clock settles."""
+    for i in range(3):
+        fn(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(iters)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(launches):
+            fn(i)
+    warm = 1
     if warm_s > 0:
-        a, b = ev[0]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        fn(0)
+        graph.replay()
         b.record()
         torch.cuda.synchronize()
-        for i in range(max(1, int(warm_s / (a.elapsed_time(b) * 1e-3)))):
-            fn(i)
-    else:
-        device_sleep(torch, 0.01 + 3e-4 * iters)
-    for i, (a, b) in enumerate(ev):
-        a.record()
-        fn(i)
-        b.record()
-    torch.cuda.synchronize()
-    return 1e3 * sum(a.elapsed_time(b) for a, b in ev) / iters   # us
+        warm = max(1, int(warm_s / (a.elapsed_time(b) * 1e-3)))
+    ms = time_replays(torch, [graph], reps, warm)
+    del graph
+    return 1e3 * ms / launches
 
 
 def gemm_bench(torch, qblk, synth, dev, iters, copies=16):
@@ -516,11 +494,8 @@ def gemm_bench(torch, qblk, synth, dev, iters, copies=16):
         if m <= 64:
             fns.append(("gemv", qblk.qblk_gemv))
         for fname, f in fns:
-            # the compute-bound 512-row case after sustained load; the short
-            # launches keep the queued form (their host launch latency would
-            # otherwise enter the event brackets)
-            us = timed_launches(torch, lambda i: f(Q4_K, wqs[i % copies], n, k, xq, m, y=y),
-                                iters, warm_s=0.25 if m == 512 else 0.0)
+            us = graph_launches(torch, lambda i: f(Q4_K, wqs[i % copies], n, k, xq, m, y=y),
+                                launches=iters, warm_s=0.1)
             ops = 2.0 * m * n * k
             row[fname] = {"us": round(us, 3), "TOPS": round(ops / (us * 1e-6) / 1e12, 2),
                           "weight_GBps": round(qblk.qblk_weight_bytes(Q4_K, n, k)
@@ -560,13 +535,11 @@ def sym_bench(torch, qblk, synth, dev):
         x = synth.torch_activations(1000 * t + 99, 1, k, device=dev)
         xq = qblk.qblk_quantize_act(x)
         y = torch.empty((1, n), dtype=torch.float32, device=dev)
-        us = timed_launches(torch, lambda i: qblk.qblk_gemv(t, wqs[i % copies], n, k, xq, 1, y=y),
-                            100)
+        us = graph_launches(torch, lambda i: qblk.qblk_gemv(t, wqs[i % copies], n, k, xq, 1, y=y))
         res[name] = {"us": round(us, 3), "weight_bytes": wb, "GBps": round(wb / (us * 1e-6) / 1e9, 1)}
         log(f"{name}: {res[name]}")
         fname = name.replace("_gemv_", "_gemv_float_")
-        us = timed_launches(torch, lambda i: qblk.qblk_gemv_float(t, wqs[i % copies], n, k, x, y=y),
-                            100)
+        us = graph_launches(torch, lambda i: qblk.qblk_gemv_float(t, wqs[i % copies], n, k, x, y=y))
         res[fname] = {"us": round(us, 3), "weight_bytes": wb, "GBps": round(wb / (us * 1e-6) / 1e9, 1)}
         log(f"{fname}: {res[fname]}")
         del wqs
@@ -612,7 +585,7 @@ def multi_bench(torch, qblk, synth, dev):
 
     res = {"weight_bytes": wb}
     for name, fn in (("three_launches", separate), ("multi_launch", multi), ("concatenated", concat)):
-        us = timed_launches(torch, fn, 60)
+        us = graph_launches(torch, fn, launches=32)
         res[name] = {"us": round(us, 3), "GBps": round(wb / (us * 1e-6) / 1e9, 1)}
     log(f"q/k/v as three matrices: {res}")
     del layers
@@ -642,8 +615,8 @@ def kv_bench(torch, qblk, synth, dev):
             del k
         qq = qblk.qblk_quantize_act(synth.torch_activations(7999, n_head, hd, device=dev))
         s = torch.empty((n_head, n_ctx), dtype=torch.float32, device=dev)
-        us = timed_launches(torch, lambda i: qblk.qblk_kv_scores(t, caches[i % copies], n_kv, n_ctx, n_ctx, hd,
-                                                                  qq, n_head, scores=s), 100)
+        us = graph_launches(torch, lambda i: qblk.qblk_kv_scores(t, caches[i % copies], n_kv, n_ctx, n_ctx, hd,
+                                                                  qq, n_head, scores=s))
         alg = cb + qblk.qblk_act_bytes(n_head, hd) + 4 * n_head * n_ctx
         res[name] = {"us": round(us, 3), "cache_bytes": cb, "alg_bytes": alg,
                      "cache_GBps": round(cb / (us * 1e-6) / 1e9, 1),
