@@ -86,7 +86,7 @@ struct GemvArgs {
   uint8_t* xq_codes;
   uint8_t* xq_ds;
   uint64_t* flags;     // [8][flag_stride] u64
-  uint32_t nslices;    // ceil(nb / 64)
+  uint32_t nslices;    // ceil(nb / 64) slices per activation row
   uint32_t flag_stride;
 };
 
@@ -107,28 +107,29 @@ __device__ __forceinline__ uint64_t launch_tag() {
 // arithmetic: one block per quad of threads, 8 elements per thread. The
 // stores are agent-scope atomic stores, which the L2 writes through to
 // memory, so they are visible to every XCD once complete.
-template <int B>
+// Slice sl covers blocks 64 (sl mod nslices) .. +63 of activation row
+// sl / nslices: one slice per workgroup-sized piece of work whatever the
+// batch, so a larger batch spreads over more producers instead of making each
+// one slower.
 __device__ __forceinline__ void quantize_slice(const GemvArgs& g, uint32_t sl) {
-  const uint32_t blk = (sl << 6) + (threadIdx.x >> 2);
+  const uint32_t b = sl / g.nslices;
+  const uint32_t blk = ((sl - b * g.nslices) << 6) + (threadIdx.x >> 2);
   const uint32_t sub = threadIdx.x & 3;
   if (blk >= g.nb) return;  // whole quads
   const uint32_t k = g.nb * 32u;
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    const float* src = g.x + b * g.ldx + 32u * blk + 8u * sub;
-    const float4 v0 = *reinterpret_cast<const float4*>(src);
-    const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-    const float e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const Q8Group q = quantize_group8(e);
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(g.xq_codes + b * k + 32u * blk + 8u * sub),
-                       static_cast<uint64_t>(q.codes.x) | static_cast<uint64_t>(q.codes.y) << 32,
+  const float* src = g.x + b * g.ldx + 32u * blk + 8u * sub;
+  const float4 v0 = *reinterpret_cast<const float4*>(src);
+  const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+  const float e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  const Q8Group q = quantize_group8(e);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(g.xq_codes + b * k + 32u * blk + 8u * sub),
+                     static_cast<uint64_t>(q.codes.x) | static_cast<uint64_t>(q.codes.y) << 32,
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (sub == 0)
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(g.xq_ds + 8u * (b * g.nb + blk)),
+                       static_cast<uint64_t>(__float_as_uint(q.d)) |
+                           static_cast<uint64_t>(static_cast<uint32_t>(q.sum)) << 32,
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (sub == 0)
-      __hip_atomic_store(reinterpret_cast<uint64_t*>(g.xq_ds + 8u * (b * g.nb + blk)),
-                         static_cast<uint64_t>(__float_as_uint(q.d)) |
-                             static_cast<uint64_t>(static_cast<uint32_t>(q.sum)) << 32,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // Producer side: workgroups below nslices quantize slices wg, wg + grid, ...
@@ -140,8 +141,8 @@ __device__ __forceinline__ void quantize_slice(const GemvArgs& g, uint32_t sl) {
 // took 3-5 us per launch on MI355X while the weight stream was running.
 template <int B>
 __device__ __forceinline__ void produce(const GemvArgs& g, uint64_t tag) {
-  for (uint32_t sl = blockIdx.x; sl < g.nslices; sl += gridDim.x) {
-    quantize_slice<B>(g, sl);
+  for (uint32_t sl = blockIdx.x; sl < B * g.nslices; sl += gridDim.x) {
+    quantize_slice(g, sl);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
     __syncthreads();
     if (threadIdx.x < 8)
@@ -164,13 +165,13 @@ __device__ __forceinline__ void wait_slices(const GemvArgs& g, uint64_t tag) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   while (true) {
     int pending = 0;
-    for (uint32_t sl = threadIdx.x; sl < g.nslices; sl += 256u)
+    for (uint32_t sl = threadIdx.x; sl < B * g.nslices; sl += 256u)
       pending |= __hip_atomic_load(f + sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag;
     if (!__syncthreads_or(pending)) return;
     const int late = __builtin_amdgcn_s_memrealtime() - t0 > 2000000ull;  // 100 MHz clock
     if (__syncthreads_or(late)) break;
   }
-  for (uint32_t sl = 0; sl < g.nslices; ++sl) quantize_slice<B>(g, sl);
+  for (uint32_t sl = 0; sl < B * g.nslices; ++sl) quantize_slice(g, sl);
   __threadfence();
   __syncthreads();
 }

@@ -56,9 +56,11 @@ inline int64_t gemv_f32_max_batch(int64_t k) { return k > 0 ? 8 : 0; }
 // caller's workspace.
 constexpr int64_t kLdsFusedMaxElems = int64_t(32) << 20;
 // Workspace of the in-launch quantization: the activation buffer (same
-// layout as qblk_quantize_act's), then 8 copies of one u64 flag per 64-block
-// slice, each copy padded to whole 128-byte lines.
-inline int64_t gemv_flag_stride(int64_t k) { return ((k / 32 + 63) / 64 + 15) / 16 * 16; }
+// layout as qblk_quantize_act's), then 8 copies of one u64 flag per (activation row,
+// 64-block slice), each copy padded to whole 128-byte lines.
+inline int64_t gemv_flag_stride(int64_t k) {  // one flag per (activation row, 64-block slice)
+  return (gemv_f32_max_batch(k) * ((k / 32 + 63) / 64) + 15) / 16 * 16;
+}
 inline int64_t gemv_flags_offset(int64_t batch, int64_t k) {
   return (batch * k + 8 * batch * (k / 32) + 255) / 256 * 256;
 }

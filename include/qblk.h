@@ -200,8 +200,9 @@ int qblk_gemv_multi(int type, const qblk_gemv_desc *descs, int count, int64_t ba
  *     rows, 64 blocks at a time, into its local memory while it streams its
  *     weight rows (work is not touched);
  *   - larger ones: the first workgroups of the launch quantize the rows once
- *     into `work` and publish each 64-block slice with a tag unique to the
- *     launch; the other workgroups issue their first weight loads, then wait
+ *     into `work`, one 64-block slice of one row each, and publish each slice
+ *     with a tag unique to the launch; the workgroups issue their first
+ *     weight loads, then wait
  *     for the tags (a bounded wait: past about 20 ms a workgroup quantizes
  *     the rows itself, so the result never depends on scheduling).
  *   x    : fp32 [batch][ldx];  other arguments as qblk_gemv.

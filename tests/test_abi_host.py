@@ -137,8 +137,9 @@ def test_gemv_f32_workspace_size_and_validation():
     for k in (32, 2048, 4096, 8192, 28672, 1 << 20):
         for b in (1, 4, 8):
             wb = qblk.qblk_gemv_f32_work_bytes(b, k)
-            # the activation buffer plus 8 copies of one 8-byte flag per 64 blocks
-            assert wb >= o.act_bytes(b, k) + 8 * 8 * (-(-k // 2048))
+            # the activation buffer plus 8 copies of one 8-byte flag per
+            # (activation row, 64-block slice)
+            assert wb >= o.act_bytes(b, k) + 8 * 8 * b * (-(-k // 2048))
             assert wb % 256 == 0
     assert qblk.qblk_gemv_f32_work_bytes(9, 4096) == 0
     assert qblk.qblk_gemv_f32_work_bytes(1, 100) == 0
