@@ -353,13 +353,15 @@ def test_gemv_f32_matches_quantize_then_gemv(wtype, n, k, batch):
 
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("n,k,batch", [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1),
-                                       (9000, 4096, 4), (3, 1 << 24, 1)])
+                                       (9000, 4096, 4), (16400, 2304, 3), (3, 1 << 24, 1),
+                                       (3, 1 << 24, 4)])
 def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
     """Matrices above 32M weights quantize the activation once per launch
-    into the workspace. One workspace serves consecutive calls on different
-    activations (a stale slice would reproduce the previous call's result),
-    also when it starts out holding arbitrary bytes; the (3, 2^24) case has
-    fewer workgroups than activation slices."""
+    into the workspace, one slice per (activation row, 64 blocks). One
+    workspace serves consecutive calls on different activations (a stale
+    slice would reproduce the previous call's result), also when it starts
+    out holding arbitrary bytes; (16400, 2304, 3) has a partial last slice in
+    every row, and the k = 2^24 cases have fewer workgroups than slices."""
     t = torch()
     print(f"gemv_f32 in-launch {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
     assert n * k > 32 << 20
