@@ -620,8 +620,10 @@ enum Mode { kQuantized = 0, kLdsFused = 1, kInLaunch = 2 };
 // Kernel variant per shape, from measurements on MI355X over the 7B- and
 // 70B-shaped Q4_K matrices (graphs of back-to-back launches): at batch 1 the
 // classic kernel with 4 rows per wave streams the largest matrices best
-// (6.0-6.5 TB/s), with 2 rows per wave the mid-size ones (activations staged
-// in LDS), 1 row per wave with 2 chunks in flight the small ones; at batch
+// (6.0-6.5 TB/s; the 7B-shaped gate/up, 28672 x 4096, with the in-launch
+// handoff 13.9 against 16.5 us with 2 rows), with 2 rows per wave the
+// mid-size ones (activations staged in LDS), 1 row per wave with 2 chunks in
+// flight the small ones; at batch
 // 2-8, 8 rows per wave above 16k rows and 4 above 3k (70B layer at batch 4:
 // 142 us against 179 us with 2 rows per wave). All variants give
 // bit-identical results.
@@ -633,11 +635,12 @@ hipError_t launch_b(const Plan& p, hipStream_t s) {
     if (n >= 8192) return launch_pipe<TYPE, B, 4, true, false>(p, s);
     return launch_pipe<TYPE, B, 2, true, false>(p, s);
   } else if constexpr (B == 1) {
-    if (n >= 16384) {
-      if (k >= 8192) return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
-      return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
-    }
+    if (n >= 16384) return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
     if (n >= 8192 && k >= 16384) return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
+    // long rows of a mid-size matrix with the in-launch handoff: two chunks
+    // per step (7B-shaped down, 4096 x 14336: 10.5 against 11.2 us; with a
+    // quantized activation one chunk stays faster, 9.7 against 10.8 us)
+    if (SYNC && n >= 3072 && n < 8192 && k >= 8192) return launch_cfg<TYPE, 1, 2, 2, SYNC>(p, s);
     if (n >= 3072) return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
     return launch_cfg<TYPE, 1, 1, 2, SYNC>(p, s);
   } else {

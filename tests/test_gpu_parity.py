@@ -353,8 +353,8 @@ def test_gemv_f32_matches_quantize_then_gemv(wtype, n, k, batch):
 
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("n,k,batch", [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1),
-                                       (9000, 4096, 4), (16400, 2304, 3), (3, 1 << 24, 1),
-                                       (3, 1 << 24, 4)])
+                                       (4096, 14336, 1), (9000, 4096, 4), (16400, 2304, 3),
+                                       (3, 1 << 24, 1), (3, 1 << 24, 4)])
 def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
     """Matrices above 32M weights quantize the activation once per launch
     into the workspace, one slice per (activation row, 64 blocks). One
