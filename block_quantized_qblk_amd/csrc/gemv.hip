@@ -783,11 +783,11 @@ hipError_t launch_gemv_multi(int type, const GemvDesc* d, int count, int64_t bat
 }
 
 // Fused quantize + GEMV (fp32 activations, batch <= gemv_f32_max_batch(k)):
-// one launch streams the weights once. Small matrices: every workgroup
-// quantizes the activation into its local memory. Larger ones: the first
-// workgroups quantize it once into the workspace and the others wait for it
-// behind their first weight loads (the per-workgroup quantization would cost
-// more than the weight stream).
+// one launch streams the weights once. Small single-row products with short
+// rows: every workgroup quantizes the activation into its local memory.
+// Otherwise the first workgroups quantize it once into the workspace and the
+// others wait for it behind their first weight loads (repeating the
+// quantization in every workgroup would cost more than the weight stream).
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
                            int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
                            hipStream_t s) {
@@ -802,7 +802,7 @@ hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const
   p.x = x;
   p.ldx = ldx;
   const int bc = static_cast<int>(batch);
-  if (n * k <= kLdsFusedMaxElems) {
+  if (gemv_f32_lds_fused(n, k, batch)) {
     p.A = make_act(nullptr, 0, k);
     return launch_type<kLdsFused>(type, bc, p, s);
   }

@@ -51,10 +51,17 @@ hipError_t launch_gemv(int type, const void* wq, int64_t n, int64_t k, const voi
 // launch (the local-memory variant keeps two 64-block slices of their codes
 // in LDS, 5 KiB per row, so the limit does not depend on k).
 inline int64_t gemv_f32_max_batch(int64_t k) { return k > 0 ? 8 : 0; }
-// Matrices of at most this many weights quantize the activation in every
-// workgroup's local memory; larger ones quantize it once per launch into the
-// caller's workspace.
-constexpr int64_t kLdsFusedMaxElems = int64_t(32) << 20;
+// Whether the fused GEMV quantizes the activation in every workgroup's local
+// memory (small single-row products with short rows) rather than once per
+// launch into the caller's workspace. Measured on MI355X (Q4_K, graphs of
+// back-to-back launches): per-workgroup quantization wins at batch 1 for
+// K <= 2048 (2048 x 2048: 3.3 against 4.4 us) and for K = 4096 up to 2048
+// rows (1024 x 4096: 4.5 against 4.7 us); the handoff wins from 4096 x 4096
+// (5.4 against 6.0 us), at K = 8192, and at every size with several rows
+// (7B-shaped q/k/v at batch 4: 9.8 against 18.2 us).
+inline bool gemv_f32_lds_fused(int64_t n, int64_t k, int64_t batch) {
+  return batch == 1 && n * k <= (int64_t(32) << 20) && (k <= 2048 || (k <= 4096 && n <= 2048));
+}
 // Workspace of the in-launch quantization: the activation buffer (same
 // layout as qblk_quantize_act's), then 8 copies of one u64 flag per (activation row,
 // 64-block slice), each copy padded to whole 128-byte lines.

@@ -196,15 +196,16 @@ int qblk_gemv_multi(int type, const qblk_gemv_desc *descs, int count, int64_t ba
  * result, bit for bit, as qblk_quantize_act(x) followed by qblk_gemv, in one
  * launch. The activation is quantized with the qblk_quantize_act rule
  * ("llama.cpp 推理引擎", §5.1 at 8 bits):
- *   - matrices of at most 32M weights: every workgroup quantizes the fp32
- *     rows, 64 blocks at a time, into its local memory while it streams its
- *     weight rows (work is not touched);
- *   - larger ones: the first workgroups of the launch quantize the rows once
+ *   - batch 1 with k <= 2048, or k <= 4096 and n <= 2048 (and at most 32M
+ *     weights): every workgroup quantizes the fp32 row, 64 blocks at a time,
+ *     into its local memory while it streams its weight rows (work is not
+ *     touched);
+ *   - otherwise: the first workgroups of the launch quantize the rows once
  *     into `work`, one 64-block slice of one row each, and publish each slice
  *     with a tag unique to the launch; the workgroups issue their first
- *     weight loads, then wait
- *     for the tags (a bounded wait: past about 20 ms a workgroup quantizes
- *     the rows itself, so the result never depends on scheduling).
+ *     weight loads, then wait for the tags (a bounded wait: past about 20 ms
+ *     a workgroup quantizes the rows itself, so the result never depends on
+ *     scheduling).
  *   x    : fp32 [batch][ldx];  other arguments as qblk_gemv.
  *   work : device workspace of qblk_gemv_f32_work_bytes(batch, k) bytes,
  *          256-byte aligned, owned by the caller. It holds no state that a

@@ -351,20 +351,27 @@ def test_gemv_f32_matches_quantize_then_gemv(wtype, n, k, batch):
         check_rel(fused[:, rows], expected(wtype, w[rows], x))
 
 
+def _in_launch(n, k, batch):
+    """Whether qblk_gemv_f32 quantizes the activation once per launch into
+    the workspace (else in every workgroup's local memory)."""
+    return not (batch == 1 and n * k <= 32 << 20 and (k <= 2048 or (k <= 4096 and n <= 2048)))
+
+
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("n,k,batch", [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1),
-                                       (4096, 14336, 1), (9000, 4096, 4), (16400, 2304, 3),
-                                       (3, 1 << 24, 1), (3, 1 << 24, 4)])
+                                       (4096, 14336, 1), (4096, 4096, 1), (1024, 4096, 2),
+                                       (9000, 4096, 4), (16400, 2304, 3), (3, 1 << 24, 1),
+                                       (3, 1 << 24, 4)])
 def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
-    """Matrices above 32M weights quantize the activation once per launch
-    into the workspace, one slice per (activation row, 64 blocks). One
+    """Products that quantize the activation once per launch into the
+    workspace, one slice per (activation row, 64 blocks). One
     workspace serves consecutive calls on different activations (a stale
     slice would reproduce the previous call's result), also when it starts
     out holding arbitrary bytes; (16400, 2304, 3) has a partial last slice in
     every row, and the k = 2^24 cases have fewer workgroups than slices."""
     t = torch()
     print(f"gemv_f32 in-launch {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
-    assert n * k > 32 << 20
+    assert _in_launch(n, k, batch)
     rng = np.random.default_rng(5 * wtype + n + k)
     w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
     wq = dev_pack(wtype, w)
