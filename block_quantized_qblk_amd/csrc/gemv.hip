@@ -641,6 +641,12 @@ hipError_t launch_b(const Plan& p, hipStream_t s) {
     // per step (7B-shaped down, 4096 x 14336: 10.5 against 11.2 us; with a
     // quantized activation one chunk stays faster, 9.7 against 10.8 us)
     if (SYNC && n >= 3072 && n < 8192 && k >= 8192) return launch_cfg<TYPE, 1, 2, 2, SYNC>(p, s);
+    // Q4_0 / Q8_0 rows (no super-block headers, fewer instructions per
+    // block) on a quantized activation: two chunks per step (Q4_0 4096 x
+    // 14336: 8.3 against 9.0 us; 4096 x 4096: 4.2 against 4.3 us; Q8_0
+    // 14336 x 4096: 13.2-14.1 against 14.2 us in two runs; Q4_K is slower
+    // this way on the 7B-shaped q/k/v and down)
+    if (MODE == kQuantized && TYPE != kQ4_K && n >= 3072) return launch_cfg<TYPE, 1, 2, 2, SYNC>(p, s);
     if (n >= 3072) return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
     return launch_cfg<TYPE, 1, 1, 2, SYNC>(p, s);
   } else {
