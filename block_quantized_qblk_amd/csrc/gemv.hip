@@ -658,7 +658,15 @@ hipError_t launch_b(const Plan& p, hipStream_t s) {
     // registers, and at batch 2-8 those re-reads bound the kernel, so the
     // larger matrices take more rows per wave
     if (n >= 16384) return launch_cfg<TYPE, B, 8, 1, SYNC>(p, s);
-    if (n >= 3072) return launch_cfg<TYPE, B, 4, 1, SYNC>(p, s);
+    if (n >= 3072) {
+      // long rows at batch 4 and above: 8 rows per wave (70B-shaped down,
+      // 8192 x 28672: 36.8 against 37.8 us at batch 4, 48.6 against 53.2 at
+      // 8; slower at batch 2); short rows: 2 (7B-shaped q/k/v, 6144 x 4096:
+      // 9.6 against 9.7 us at batch 4, 13.6 against 14.7 at 8)
+      if (B >= 4 && k >= 16384) return launch_cfg<TYPE, B, 8, 1, SYNC>(p, s);
+      if (k <= 4096) return launch_cfg<TYPE, B, 2, 1, SYNC>(p, s);
+      return launch_cfg<TYPE, B, 4, 1, SYNC>(p, s);
+    }
     return launch_cfg<TYPE, B, 1, 1, SYNC>(p, s);
   }
 }
