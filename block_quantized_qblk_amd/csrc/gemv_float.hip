@@ -15,8 +15,11 @@
 // Mapping as in the quantized GEMV: a wave owns R weight rows and walks them
 // in chunks of 64 blocks, lane l taking block c + l with one 16-byte
 // (nibbles) or two (Q8_0) nontemporal loads per row; the lane's 32 activations
-// of that block are read once per batch row (8 float4 loads, L2-resident) and
-// shared by the R rows. A DPP wave reduction ends each (row, batch) sum.
+// of that block are read once per batch row (8 float4 loads) and shared by the
+// R rows. When they fit in 32 KiB the workgroup first copies the activation
+// rows into LDS, so its four waves read them from there rather than each from
+// L2 (Q8_0 14336 x 4096: 17.4 against 22.4 us). A DPP wave reduction ends each
+// (row, batch) sum.
 #include "qblk_device.h"
 
 namespace qblk {
@@ -115,15 +118,40 @@ __device__ __forceinline__ float block_dot(const FBlock<TYPE>& f, const float4 (
   return s;
 }
 
-template <int TYPE, int R, int B>
+// LDS bytes of the staged activation rows: B rows of nb blocks, each block's
+// 32 floats as 8 float4 units laid out unit-major per 64-block chunk, so
+// that a wave's read of unit i of 64 consecutive blocks is one contiguous
+// KiB (lane l at +16 l, free of bank conflicts).
+__host__ __device__ inline uint32_t xlds_bytes(int b, int64_t nb) {
+  return static_cast<uint32_t>(b * ((nb + 63) / 64) * 64 * 128);
+}
+constexpr uint32_t kXLdsMax = 32768;
+
+template <int TYPE, int R, int B, bool XLDS>
 __global__ __launch_bounds__(64 * kWaves) void gemv_float_kernel(WeightView W, int64_t n, int64_t nb,
                                                                   const float* __restrict__ x, int64_t ldx,
                                                                   int batch, float* __restrict__ y,
                                                                   int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) float4 xs[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * R;
-  if (row0 >= n) return;  // wave-uniform; the kernel has no workgroup barrier
+  const int64_t nc = (nb + 63) / 64;  // 64-block chunks per row
+  if constexpr (XLDS) {
+    // the workgroup copies the activation rows into LDS once: float4 unit u
+    // of block blk of row b goes to ((b * nc + blk / 64) * 8 + u) * 64 + blk % 64
+    for (int b = 0; b < B; ++b) {
+      const int bb = b < batch ? b : batch - 1;
+      const float4* xp = reinterpret_cast<const float4*>(x + bb * ldx);
+      for (int64_t q = threadIdx.x; q < nb * 8; q += 64 * kWaves) {
+        const int64_t blk = q >> 3;
+        const int u = static_cast<int>(q & 7);
+        xs[((b * nc + (blk >> 6)) * 8 + u) * 64 + (blk & 63)] = xp[q];
+      }
+    }
+    __syncthreads();
+  }
+  if (row0 >= n) return;  // wave-uniform; no workgroup barrier follows
 
   float acc[R][B];
 #pragma unroll
@@ -143,10 +171,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_float_kernel(WeightView W, i
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const int bb = b < batch ? b : batch - 1;  // padded batch rows are not stored
-        const float4* xp = reinterpret_cast<const float4*>(x + bb * ldx + 32 * blk);
         float4 xv[8];
+        if constexpr (XLDS) {
+          const float4* xl = xs + (b * nc + (c >> 6)) * 512 + lane;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xv[i] = xp[i];
+          for (int i = 0; i < 8; ++i) xv[i] = xl[64 * i];
+        } else {
+          const float4* xp = reinterpret_cast<const float4*>(x + bb * ldx + 32 * blk);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[i] = xp[i];
+        }
         float sx = 0.0f;
         if constexpr (TYPE != kQ8_0) {
 #pragma unroll
@@ -177,8 +211,13 @@ void launch_rb(const WeightView& W, int64_t n, int64_t nb, const float* x, int64
                int64_t ldy, hipStream_t s) {
   const int64_t rows_per_wg = static_cast<int64_t>(kWaves) * R;
   const dim3 grid(static_cast<uint32_t>((n + rows_per_wg - 1) / rows_per_wg));
-  hipLaunchKernelGGL((gemv_float_kernel<TYPE, R, B>), grid, dim3(64 * kWaves), 0, s, W, n, nb, x, ldx, batch,
-                     y, ldy);
+  const uint32_t lds = xlds_bytes(B, nb);
+  if (lds <= kXLdsMax)
+    hipLaunchKernelGGL((gemv_float_kernel<TYPE, R, B, true>), grid, dim3(64 * kWaves), lds, s, W, n, nb, x,
+                       ldx, batch, y, ldy);
+  else
+    hipLaunchKernelGGL((gemv_float_kernel<TYPE, R, B, false>), grid, dim3(64 * kWaves), 0, s, W, n, nb, x,
+                       ldx, batch, y, ldy);
 }
 
 template <int TYPE>
