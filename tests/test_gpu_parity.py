@@ -419,7 +419,7 @@ def _float_expected(wtype, w, x):
 
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("n,k,batch", [(37, 1024, 1), (300, 4096, 2), (129, 2304, 3), (70, 256, 8),
-                                       (1000, 8192, 1), (65, 512, 11)])
+                                       (1000, 8192, 1), (65, 512, 11), (40, 28672, 1), (50, 4096, 8)])
 def test_gemv_float_random(wtype, n, k, batch):
     print(f"gemv float {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
     rng = np.random.default_rng(91 * wtype + n + batch)
