@@ -187,9 +187,9 @@ QBLK_EXPORT int qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const 
   const int st = check_product(type, wq, n, k, xq, m, y, ldy);
   if (st != QBLK_OK || n == 0 || m == 0) return st;
   // grid: x = n / 128 workgroups of 256 work-items, y = m / 128 (<= 65535),
-  // or, for m <= 64, x = n / 32; a workgroup addresses its activation and
+  // or, for m <= 64, x = n / 64; a workgroup addresses its activation and
   // weight rows with 32-bit offsets, so k is limited to 2^24
-  const int64_t wgs = m <= qblk::kGemmSmallMaxRows ? (n + 31) / 32 : (n + 127) / 128;
+  const int64_t wgs = m <= qblk::kGemmSmallMaxRows ? (n + 63) / 64 : (n + 127) / 128;
   if (256 * wgs > kMaxGridThreads || (m + 127) / 128 > 65535 || k > kMaxGemmK)
     return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
