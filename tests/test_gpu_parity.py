@@ -497,7 +497,8 @@ def test_kv_store_bit_exact(wtype):
 @pytest.mark.parametrize("wtype", KV_TYPES)
 @pytest.mark.parametrize("n_kv,n_head,hd,n_ctx,n_tok", [(1, 1, 128, 64, 1), (2, 8, 128, 300, 257),
                                                         (4, 8, 64, 100, 100), (2, 16, 256, 50, 33),
-                                                        (3, 6, 128, 80, 45)])
+                                                        (3, 6, 128, 80, 45), (2, 10, 64, 700, 650),
+                                                        (1, 7, 256, 40, 40)])
 def test_kv_scores_random(wtype, n_kv, n_head, hd, n_ctx, n_tok):
     print(f"kv scores {TNAME[wtype]} n_kv={n_kv} n_head={n_head} hd={hd} n_tok={n_tok}", flush=True)
     rng = np.random.default_rng(130 + wtype + n_tok)
