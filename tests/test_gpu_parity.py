@@ -498,7 +498,8 @@ def test_kv_store_bit_exact(wtype):
 @pytest.mark.parametrize("n_kv,n_head,hd,n_ctx,n_tok", [(1, 1, 128, 64, 1), (2, 8, 128, 300, 257),
                                                         (4, 8, 64, 100, 100), (2, 16, 256, 50, 33),
                                                         (3, 6, 128, 80, 45), (2, 10, 64, 700, 650),
-                                                        (1, 7, 256, 40, 40)])
+                                                        (1, 7, 256, 40, 40), (16, 64, 64, 8300, 8200),
+                                                        (32, 32, 256, 4200, 4100)])
 def test_kv_scores_random(wtype, n_kv, n_head, hd, n_ctx, n_tok):
     print(f"kv scores {TNAME[wtype]} n_kv={n_kv} n_head={n_head} hd={hd} n_tok={n_tok}", flush=True)
     rng = np.random.default_rng(130 + wtype + n_tok)
@@ -533,18 +534,23 @@ def test_kv_scores_prefix_and_stores_agree():
     assert np.all(host(s) == -1.0)
 
 
-def test_kv_scores_70b_shape_sampled():
+@pytest.mark.parametrize("wtype", KV_TYPES)
+@pytest.mark.parametrize("n_ctx,n_tok", [(8192, 8192), (20000, 16411)])
+def test_kv_scores_70b_shape_sampled(wtype, n_ctx, n_tok):
     """70B-shaped decode step: 64 query heads over 8 KV heads of 128, 8192
-    cached tokens, Q8_0; the oracle checks sampled tokens of every head."""
-    print("kv scores 70B shape", flush=True)
-    rng = np.random.default_rng(150)
-    n_kv, n_head, hd, n_ctx = 8, 64, 128, 8192
-    k = rng.standard_normal((n_kv, n_ctx, hd)).astype(np.float32)
+    cached tokens, or 16411 of 20000 (over 2^17 cache rows, where Q8_0 takes
+    two token steps per wave, with a ragged last workgroup); the oracle checks
+    sampled tokens of every head."""
+    print(f"kv scores 70B shape {TNAME[wtype]} n_tok={n_tok}", flush=True)
+    rng = np.random.default_rng(150 + wtype)
+    n_kv, n_head, hd = 8, 64, 128
+    k = rng.standard_normal((n_kv, n_tok, hd)).astype(np.float32)
     q = rng.standard_normal((n_head, hd)).astype(np.float32)
-    cache = _kv_fill(o.TYPE_Q8_0, k, n_ctx)
-    s = host(qblk.qblk_kv_scores(o.TYPE_Q8_0, cache, n_kv, n_ctx, n_ctx, hd, dev_quantize(q), n_head))
-    toks = _sample_rows(n_ctx, 200, 151)
-    check_rel(s[:, toks], o.kv_scores(o.TYPE_Q8_0, k[:, toks], q, n_head)[1])
+    cache = _kv_fill(wtype, k, n_ctx)
+    s = host(qblk.qblk_kv_scores(wtype, cache, n_kv, n_ctx, n_tok, hd, dev_quantize(q), n_head))
+    assert s.shape == (n_head, n_tok)
+    toks = np.unique(np.concatenate([_sample_rows(n_tok, 200, 151), np.arange(n_tok - 70, n_tok)]))
+    check_rel(s[:, toks], o.kv_scores(wtype, k[:, toks], q, n_head)[1])
 
 
 # ================================================================ multi-product launch
