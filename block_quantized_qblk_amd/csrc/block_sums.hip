@@ -23,9 +23,9 @@ __global__ __launch_bounds__(256) void block_sums_kernel(WeightView W, int64_t n
   const uint4 a1 = load16(ap + 16);
   int S;
   if constexpr (TYPE == kQ8_0) {
-    S = dot_i8x32(load16(wquant + 32 * blk), load16(wquant + 32 * blk + 16), a0, a1, 0);
+    S = dot_i8x32(load16(wquant + 32 * blk), load16(wquant + 32 * blk + 16), a0, a1);
   } else {
-    S = dot_nib32(load16(wquant + 16 * blk), a0, a1, 0);
+    S = dot_nib32(load16(wquant + 16 * blk), a0, a1);
     if constexpr (TYPE == kQ4_0 || TYPE == kQ4_0H) S -= 8 * __float_as_int(A.dsum(mm, blk).y);
   }
   out[gid] = S;

@@ -190,20 +190,20 @@ __device__ __forceinline__ void block_fma(uint32_t lane, const WChunk<TYPE>& w,
     const float wm = half_bits_to_float(s.h.x >> 16) * static_cast<float>(q4k_mn(s.h, j));
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int S = dot_nib32(w.q, a[b][u][0], a[b][u][1], 0);
+      const int S = dot_nib32(w.q, a[b][u][0], a[b][u][1]);
       const float asum = static_cast<float>(__float_as_int(ds[b][u].y));
       acc[b] = fmaf(ds[b][u].x, fmaf(sw, static_cast<float>(S), wm * asum), acc[b]);
     }
   } else if constexpr (TYPE == kQ4_0 || TYPE == kQ4_0H) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int S = dot_nib32(w.q, a[b][u][0], a[b][u][1], 0) - 8 * __float_as_int(ds[b][u].y);
+      const int S = dot_nib32(w.q, a[b][u][0], a[b][u][1]) - 8 * __float_as_int(ds[b][u].y);
       acc[b] = fmaf(s.d * ds[b][u].x, static_cast<float>(S), acc[b]);
     }
   } else {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int S = dot_i8x32(w.q0, w.q1, a[b][u][0], a[b][u][1], 0);
+      const int S = dot_i8x32(w.q0, w.q1, a[b][u][0], a[b][u][1]);
       acc[b] = fmaf(s.d * ds[b][u].x, static_cast<float>(S), acc[b]);
     }
   }

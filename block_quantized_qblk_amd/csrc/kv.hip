@@ -110,13 +110,13 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const uint8_t* __restric
       for (int it = 0; it < kIter; ++it) {
         int s;
         if constexpr (kHalf) {
-          s = dot4(kc[it].x, qa0.x, 0);
+          s = dot4_zero(kc[it].x, qa0.x);
           s = dot4(kc[it].y, qa0.y, s);
           s = dot4(kc[it].z, qa0.z, s);
           s = dot4(kc[it].w, qa0.w, s);
           s += quad_swap<kQuadXor1>(s);  // the block's other half (exact)
         } else {
-          s = dot_nib32(kc[it], qa0, qa1, 0) - 8 * __float_as_int(ds.y);  // codes are nibble - 8
+          s = dot_nib32(kc[it], qa0, qa1) - 8 * __float_as_int(ds.y);  // codes are nibble - 8
         }
         float v = static_cast<float>(s) * dk[it] * ds.x;
         // sum over the token's blocks: lanes hold one block each (Q4_0) or
