@@ -283,3 +283,101 @@ def test_q4_0_f16_round_trip_bound_and_ranges():
     assert np.all(err <= bound)
     # the stored scale is an fp16 value
     assert np.array_equal(np.asarray(d).astype(np.float16).astype(np.float32), d)
+
+
+# ---------------------------------------------------------------- Q4_K code choices (reading R8)
+
+def _f16_value(bits):
+    """fp16 bit patterns -> fp64 values, through NumPy's own binary16 type."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def _f16_prev(bits):
+    """The next smaller fp16 value of non-negative, non-zero patterns: the
+    bit pattern stepped down by one."""
+    return _f16_value(np.asarray(bits, np.int64) - 1)
+
+
+def _q4_k_minimality(w, enc):
+    """Checks the R8 choices of one encoding against the raw fp32 rows:
+    every code and super-block scale covers its sub-block ([P2] §5.2 range
+    hi - lo split into 15 steps, zero point -M_j <= lo_j) and is the smallest
+    one that does. Recomputes m_j, hi_j and t_j from the input, not from the
+    oracle's intermediate values."""
+    x = np.asarray(w, np.float64)
+    N, K = x.shape
+    xs = x.reshape(N, K // 256, 8, 32)
+    hi = xs.max(-1)
+    m = np.maximum(0.0, -xs.min(-1))
+    dmp_bits = np.asarray(enc["dmin_bits"], np.int64) & 0x7FFF
+    dmp = _f16_value(dmp_bits)
+    d_bits = np.asarray(enc["d_bits"], np.int64)
+    d = _f16_value(d_bits)
+    sc, mn = enc["sc"], enc["mn"]
+    mmax = m.max(-1)
+    # d_min: covers (63 * dmin+ >= max m_j), and one fp16 step less does not
+    assert np.all(63 * dmp >= mmax)
+    pos = dmp_bits > 0
+    assert np.all(63 * _f16_prev(np.where(pos, dmp_bits, 1))[pos] < mmax[pos])
+    assert np.all(mmax[~pos] == 0)
+    # mn_j: covers, and mn_j - 1 does not
+    Mj = mn * dmp[..., None]
+    assert np.all(Mj >= m)
+    assert np.all(((mn - 1) * dmp[..., None] < m)[mn > 0])
+    assert np.all(mn[m == 0] == 0)
+    # d: 945 d >= max t_j with t_j = hi_j + M_j, and one fp16 step less does not
+    t = hi + Mj
+    tmax = t.max(-1)
+    assert np.all(945 * d >= tmax)
+    dp = d_bits > 0
+    assert np.all(945 * _f16_prev(np.where(dp, d_bits, 1))[dp] < tmax[dp])
+    assert np.all(tmax[~dp] <= 0)
+    # sc_j: covers (15 sc_j d >= t_j), and sc_j - 1 does not
+    assert np.all(15 * sc * d[..., None] >= t)
+    assert np.all((15 * (sc - 1) * d[..., None] < t)[sc > 0])
+
+
+def _minimality_inputs():
+    rng = np.random.default_rng(71)
+    sets = [_blocks_with_special_cases(rng, 24, 2048)]
+    pos = np.abs(rng.standard_normal((4, 512))).astype(np.float32) * 0.02
+    sets.append(pos)                       # all-positive super-blocks
+    sets.append(-pos)                      # all-negative super-blocks
+    sets.append((rng.standard_t(5, (8, 1024)) * 0.02 / np.sqrt(5 / 3)).astype(np.float32))
+    # ranges spanning many binades, from tiny to large super-blocks
+    sets.append((rng.standard_normal((8, 256)) * np.logspace(-6, 3, 8)[:, None]).astype(np.float32))
+    return sets
+
+
+def test_q4_k_codes_are_the_smallest_covering_ones():
+    """Reading R8 pinned directly: d_min, mn_j, d and sc_j are each the
+    smallest value that covers its sub-blocks, on seeded rows with special
+    blocks, all-positive and all-negative super-blocks, heavy tails and
+    scales from 1e-6 to 1e3."""
+    for w in _minimality_inputs():
+        _q4_k_minimality(w, o.quantize_q4_k(w))
+
+
+def test_q4_k_hand_computed_super_block():
+    """One super-block worked out by hand from [P2] §5.2/§5.5 and reading
+    R8 (tests/golden/q4_k_hand_superblock.json, derivation in its note):
+    d, d_min, the 8 scale and min codes and the codes of every element."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "q4_k_hand_superblock.json")))
+    w = np.zeros((1, 256), np.float32)
+    for j in range(8):
+        w[0, 32 * j] = g["lo"][j]
+        w[0, 32 * j + 1] = g["hi"][j]
+    enc = o.quantize_q4_k(w)
+    assert int(enc["d_bits"][0, 0]) == g["d_bits"]
+    assert int(enc["dmin_bits"][0, 0]) == g["dmin_bits"]
+    assert enc["sc"][0, 0].tolist() == g["sc"]
+    assert enc["mn"][0, 0].tolist() == g["mn"]
+    q = enc["q"][0].reshape(8, 32)
+    assert q[:, 0].tolist() == g["q_lo"]
+    assert q[:, 1].tolist() == g["q_hi"]
+    for j in range(8):
+        assert np.all(q[j, 2:] == g["q_zero"][j]), j
+    _q4_k_minimality(w, enc)

@@ -192,3 +192,51 @@ def test_mutant_kv_head_interleaved_is_caught(monkeypatch):
     monkeypatch.setattr(o, "kv_scores", interleaved)
     with pytest.raises(AssertionError):
         pins.test_kv_scores_group_structure()
+
+
+def _bump_codes(monkeypatch, field):
+    """quantize_q4_k choosing a code one larger than needed wherever it can
+    (a larger code still covers the sub-block, so the round-trip bound
+    relative to the chosen scale still holds)."""
+    orig = o.quantize_q4_k
+
+    def mutant(w):
+        enc = orig(w)
+        c = enc[field]
+        enc[field] = np.where((c > 0) & (c < 63), c + 1, c)
+        # codes re-taken against the changed scale and zero point, as an
+        # encoder making this choice would ([P2] §5.2 step)
+        x = np.asarray(w, np.float64).reshape(enc["sc"].shape + (32,))
+        S = enc["sc"] * o.f16_bits_to_f64(enc["d_bits"])[..., None]
+        M = -enc["mn"] * o.f16_bits_to_f64(enc["dmin_bits"])[..., None]
+        q = np.clip(o.round_half_away((x + M[..., None]) / np.where(S == 0, 1, S)[..., None]), 0, 15)
+        enc["q"] = np.where((S == 0)[..., None], 0, q).astype(np.int64).reshape(enc["q"].shape)
+        return enc
+    monkeypatch.setattr(o, "quantize_q4_k", mutant)
+
+
+def test_mutant_q4_k_scale_code_one_too_large_is_caught(monkeypatch):
+    _bump_codes(monkeypatch, "sc")
+    inv.test_q4_k_round_trip_bound_and_ranges()      # not caught by the bound
+    with pytest.raises(AssertionError):
+        inv.test_q4_k_codes_are_the_smallest_covering_ones()
+
+
+def test_mutant_q4_k_min_code_one_too_large_is_caught(monkeypatch):
+    _bump_codes(monkeypatch, "mn")
+    with pytest.raises(AssertionError):
+        inv.test_q4_k_codes_are_the_smallest_covering_ones()
+
+
+@pytest.mark.parametrize("right,wrong", [(945, 900), (63, 60)])
+def test_mutant_q4_k_super_block_divisor_is_caught(monkeypatch, right, wrong):
+    """d from max t_j / (15 * 60) instead of / (15 * 63), or d_min from
+    max m_j / 60 instead of / 63: larger super-block scales that still cover
+    every sub-block."""
+    orig = o.f16_ceil_div
+    monkeypatch.setattr(o, "f16_ceil_div", lambda v, c: orig(v, wrong if c == right else c))
+    inv.test_q4_k_round_trip_bound_and_ranges()      # not caught by the bound
+    with pytest.raises(AssertionError):
+        inv.test_q4_k_codes_are_the_smallest_covering_ones()
+    with pytest.raises(AssertionError):
+        inv.test_q4_k_hand_computed_super_block()
