@@ -422,6 +422,29 @@ def traffic_probe(torch, qblk, synth, dev):
                       "gemm_sources_sha256": sources_sha256(GEMM_SOURCES)}))
 
 
+def gemv_launches(synth):
+    """(type, n, k, batch, fused) of every GEMV product this benchmark times
+    (fused: qblk_gemv_f32; else qblk_gemv on a quantized activation). The
+    kernel instance each one runs must be run by a parity case too."""
+    Q4_0, Q8_0, Q4_K = 1, 2, 3
+    out = set()
+    for shapes, batches in ((synth.LAYER_70B, (1, 4)), (synth.LAYER_7B, (1,))):
+        dims = {name: (n, k) for name, n, k in shapes}
+        groups = [(dims["q"][0] + dims["k"][0] + dims["v"][0], dims["q"][1]), dims["o"],
+                  (dims["gate"][0] + dims["up"][0], dims["gate"][1]), dims["down"]]
+        for n, k in groups:
+            for b in batches:
+                out.add((Q4_K, n, k, b, True))
+            if shapes is synth.LAYER_70B:
+                out.add((Q4_K, n, k, 1, False))       # the two-step token
+    for m in (1, 8, 64):                                # decode/prefill crossover
+        out.add((Q4_K, 14336, 4096, m, False))
+    out.add((Q4_0, 4096, 4096, 1, False))
+    out.add((Q8_0, 14336, 4096, 1, False))
+    out.add((Q4_K, 10240, 8192, 1, False))            # q/k/v concatenated, one launch
+    return sorted(out)
+
+
 def m_bytes(qblk, synth, layers):
     return layers * sum(qblk.qblk_weight_bytes(qblk.Q4_K, n, k) for _, n, k in synth.LAYER_70B)
 

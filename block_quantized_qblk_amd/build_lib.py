@@ -23,6 +23,7 @@ SOURCES = [
     "quantize_act.hip",
     "pack_weights.hip",
     "gemv.hip",
+    "gemv_select.cpp",
     "gemv_float.hip",
     "gemm.hip",
     "gemm_small.hip",

@@ -32,7 +32,7 @@ constexpr int64_t kMaxGridThreads = (int64_t{1} << 32) - 256;
 
 static_assert(QBLK_GEMV_MULTI_MAX == qblk::kGemvMultiMax, "descriptor list sizes agree");
 
-int finish(hipError_t e) {
+qblk_status finish(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
     return QBLK_ERR_LAUNCH;
@@ -41,7 +41,7 @@ int finish(hipError_t e) {
 }
 
 // Shared validation of the product entry points.
-int check_product(int type, const void* wq, int64_t n, int64_t k, const void* xq, int64_t m,
+qblk_status check_product(int type, const void* wq, int64_t n, int64_t k, const void* xq, int64_t m,
                   const void* out, int64_t ldy) {
   if (!valid_type(type)) return QBLK_ERR_ARG;
   if (n < 0 || m < 0) return QBLK_ERR_ARG;
@@ -55,7 +55,7 @@ int check_product(int type, const void* wq, int64_t n, int64_t k, const void* xq
 
 }  // namespace
 
-QBLK_EXPORT int qblk_abi_version(void) { return QBLK_ABI_VERSION; }
+QBLK_EXPORT int qblk_abi_version(void) { return QBLK_VERSION; }
 
 QBLK_EXPORT const char* qblk_strerror(int status) {
   switch (status) {
@@ -86,7 +86,7 @@ QBLK_EXPORT size_t qblk_act_bytes(int64_t m, int64_t k) {
   return static_cast<size_t>(m * k + 8 * m * (k / 32));
 }
 
-QBLK_EXPORT int qblk_pack_weights(int type, const float* w, int64_t n, int64_t k, int64_t ldw,
+QBLK_EXPORT qblk_status qblk_pack_weights(int type, const float* w, int64_t n, int64_t k, int64_t ldw,
                                   void* wq, hipStream_t stream) {
   if (!valid_type(type) || n < 0) return QBLK_ERR_ARG;
   if (!valid_k(type, k)) return QBLK_ERR_SHAPE;
@@ -99,7 +99,7 @@ QBLK_EXPORT int qblk_pack_weights(int type, const float* w, int64_t n, int64_t k
   return finish(qblk::launch_pack_weights(type, w, n, k, ldw, wq, qblk::row_bytes(type, k), stream));
 }
 
-QBLK_EXPORT int qblk_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, void* xq,
+QBLK_EXPORT qblk_status qblk_quantize_act(const float* x, int64_t m, int64_t k, int64_t ldx, void* xq,
                                   hipStream_t stream) {
   if (m < 0) return QBLK_ERR_ARG;
   if (k <= 0 || k % 32 != 0) return QBLK_ERR_SHAPE;
@@ -112,9 +112,9 @@ QBLK_EXPORT int qblk_quantize_act(const float* x, int64_t m, int64_t k, int64_t 
   return finish(qblk::launch_quantize_act(x, m, k, ldx, xq, stream));
 }
 
-QBLK_EXPORT int qblk_gemv(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+QBLK_EXPORT qblk_status qblk_gemv(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                           int64_t batch, float* y, int64_t ldy, hipStream_t stream) {
-  const int st = check_product(type, wq, n, k, xq, batch, y, ldy);
+  const qblk_status st = check_product(type, wq, n, k, xq, batch, y, ldy);
   if (st != QBLK_OK || n == 0 || batch == 0) return st;
   if (batch > QBLK_GEMV_MAX_BATCH) return QBLK_ERR_UNSUPPORTED;
   if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
@@ -133,10 +133,10 @@ QBLK_EXPORT size_t qblk_gemv_f32_work_bytes(int64_t batch, int64_t k) {
   return static_cast<size_t>(qblk::gemv_f32_work_bytes(batch, k));
 }
 
-QBLK_EXPORT int qblk_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
+QBLK_EXPORT qblk_status qblk_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
                               int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
                               hipStream_t stream) {
-  const int st = check_product(type, wq, n, k, x, batch, y, ldy);
+  const qblk_status st = check_product(type, wq, n, k, x, batch, y, ldy);
   if (st != QBLK_OK || n == 0 || batch == 0) return st;
   if (work == nullptr) return QBLK_ERR_ARG;
   if (ldx < k) return QBLK_ERR_SHAPE;
@@ -147,7 +147,19 @@ QBLK_EXPORT int qblk_gemv_f32(int type, const void* wq, int64_t n, int64_t k, co
   return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, work, stream));
 }
 
-QBLK_EXPORT int qblk_gemv_multi(int type, const qblk_gemv_desc* descs, int count, int64_t batch,
+QBLK_EXPORT qblk_status qblk_gemv_variant(int type, int64_t n, int64_t k, int64_t batch, int fused,
+                                  char* name, size_t len) {
+  if (!valid_type(type) || n <= 0 || batch <= 0 || name == nullptr || len == 0) return QBLK_ERR_ARG;
+  if (!valid_k(type, k)) return QBLK_ERR_SHAPE;
+  if (batch > (fused ? qblk::gemv_f32_max_batch(k) : QBLK_GEMV_MAX_BATCH)) return QBLK_ERR_UNSUPPORTED;
+  const int b = static_cast<int>(batch < 8 ? batch : 8);
+  const int mode = !fused ? qblk::kGemvQuantized
+                          : (qblk::gemv_f32_lds_fused(n, k, batch) ? qblk::kGemvLdsFused : qblk::kGemvInLaunch);
+  const int w = qblk::gemv_variant_name(qblk::select_gemv(type, n, k, b, mode), name, len);
+  return w > 0 && static_cast<size_t>(w) < len ? QBLK_OK : QBLK_ERR_ARG;
+}
+
+QBLK_EXPORT qblk_status qblk_gemv_multi(int type, const qblk_gemv_desc* descs, int count, int64_t batch,
                                 hipStream_t stream) {
   if (!valid_type(type) || count < 0 || batch < 0) return QBLK_ERR_ARG;
   if (count == 0 || batch == 0) return QBLK_OK;
@@ -156,7 +168,7 @@ QBLK_EXPORT int qblk_gemv_multi(int type, const qblk_gemv_desc* descs, int count
   int64_t wgs = 0;
   for (int i = 0; i < count; ++i) {
     const qblk_gemv_desc& d = descs[i];
-    const int st = check_product(type, d.wq, d.n, d.k, d.xq, batch, d.y, d.ldy);
+    const qblk_status st = check_product(type, d.wq, d.n, d.k, d.xq, batch, d.y, d.ldy);
     if (st != QBLK_OK) return st;
     wgs += (d.n + 7) / 8;  // at most 2 rows per wave, 4 waves per workgroup
   }
@@ -169,10 +181,10 @@ QBLK_EXPORT int qblk_gemv_multi(int type, const qblk_gemv_desc* descs, int count
   return finish(qblk::launch_gemv_multi(type, d, count, batch, stream));
 }
 
-QBLK_EXPORT int qblk_gemv_float(int type, const void* wq, int64_t n, int64_t k, const float* x,
+QBLK_EXPORT qblk_status qblk_gemv_float(int type, const void* wq, int64_t n, int64_t k, const float* x,
                                 int64_t ldx, int64_t batch, float* y, int64_t ldy,
                                 hipStream_t stream) {
-  const int st = check_product(type, wq, n, k, x, batch, y, ldy);
+  const qblk_status st = check_product(type, wq, n, k, x, batch, y, ldy);
   if (st != QBLK_OK || n == 0 || batch == 0) return st;
   if (ldx < k) return QBLK_ERR_SHAPE;
   if (ldx % 4 != 0) return QBLK_ERR_ALIGN;
@@ -182,9 +194,9 @@ QBLK_EXPORT int qblk_gemv_float(int type, const void* wq, int64_t n, int64_t k, 
   return finish(qblk::launch_gemv_float(type, wq, n, k, x, ldx, batch, y, ldy, stream));
 }
 
-QBLK_EXPORT int qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+QBLK_EXPORT qblk_status qblk_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                           int64_t m, float* y, int64_t ldy, hipStream_t stream) {
-  const int st = check_product(type, wq, n, k, xq, m, y, ldy);
+  const qblk_status st = check_product(type, wq, n, k, xq, m, y, ldy);
   if (st != QBLK_OK || n == 0 || m == 0) return st;
   // grid: x = n / 128 workgroups of 256 work-items, y = m / 128 (<= 65535),
   // or, for m <= 64, x = n / 64; a workgroup addresses its activation and
@@ -210,7 +222,7 @@ QBLK_EXPORT size_t qblk_kv_cache_bytes(int type, int64_t n_kv, int64_t n_ctx, in
   return static_cast<size_t>(n_kv * n_ctx * qblk::row_bytes(type, head_dim));
 }
 
-QBLK_EXPORT int qblk_kv_store(int type, const float* x, int64_t n_kv, int64_t head_dim, int64_t ldx,
+QBLK_EXPORT qblk_status qblk_kv_store(int type, const float* x, int64_t n_kv, int64_t head_dim, int64_t ldx,
                               void* cache, int64_t n_ctx, int64_t pos, hipStream_t stream) {
   if (!(type == QBLK_Q4_0 || type == QBLK_Q8_0 || type == QBLK_Q4_0_F16) || n_kv < 0) return QBLK_ERR_ARG;
   if (!valid_kv(type, head_dim) || n_ctx <= 0 || pos < 0 || pos >= n_ctx) return QBLK_ERR_SHAPE;
@@ -225,7 +237,7 @@ QBLK_EXPORT int qblk_kv_store(int type, const float* x, int64_t n_kv, int64_t he
                                           n_ctx * rb, stream));
 }
 
-QBLK_EXPORT int qblk_kv_scores(int type, const void* cache, int64_t n_kv, int64_t n_ctx, int64_t n_tok,
+QBLK_EXPORT qblk_status qblk_kv_scores(int type, const void* cache, int64_t n_kv, int64_t n_ctx, int64_t n_tok,
                                int64_t head_dim, const void* q, int64_t n_head, float* scores, int64_t lds,
                                hipStream_t stream) {
   if (!(type == QBLK_Q4_0 || type == QBLK_Q8_0 || type == QBLK_Q4_0_F16)) return QBLK_ERR_ARG;
@@ -240,9 +252,9 @@ QBLK_EXPORT int qblk_kv_scores(int type, const void* cache, int64_t n_kv, int64_
   return finish(qblk::launch_kv_scores(type, cache, n_kv, n_ctx, n_tok, head_dim, q, n_head, scores, lds, stream));
 }
 
-QBLK_EXPORT int qblk_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,
+QBLK_EXPORT qblk_status qblk_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                                 int64_t m, int32_t* sums, hipStream_t stream) {
-  const int st = check_product(type, wq, n, k, xq, m, sums, n);
+  const qblk_status st = check_product(type, wq, n, k, xq, m, sums, n);
   if (st != QBLK_OK || n == 0 || m == 0) return st;
   if (m * n * (k / 32) > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();

@@ -217,16 +217,7 @@ __device__ __forceinline__ void block_fma(uint32_t lane, const WChunk<TYPE>& w,
 // of its 64 blocks, then the second 16 (a lane's 16-B read is then
 // contiguous with its neighbours', free of bank conflicts); after the B rows
 // of codes the (d, sum) pairs, [B][nb].
-__host__ __device__ inline uint32_t act_lds_row(uint32_t nb) { return ((nb + 63u) >> 6) * 2048u; }
-__host__ __device__ inline uint32_t act_lds_bytes(int b, uint32_t nb) {
-  return static_cast<uint32_t>(b) * (act_lds_row(nb) + 8u * nb);
-}
-// LDS bytes per workgroup up to which the activations are staged: 16 KiB
-// for one activation row (70B-shaped down, 36 KiB: 26.9 us staged against
-// 24.6 us read from L2), 40 KiB for several (70B-shaped gate/up at batch 4,
-// 40 KiB: 59.8 against 62.1 us)
-constexpr uint32_t kActLdsMax = 16384;
-constexpr uint32_t kActLdsMaxBatch = 40960;
+// (act_lds_row, act_lds_bytes and the staging limits: qblk_internal.h)
 
 template <int B>
 __device__ __forceinline__ void stage_acts(const GemvArgs& g, uint8_t* smem) {
@@ -587,9 +578,7 @@ inline dim3 grid_for(int64_t n) {
 }
 
 // The activation rows are staged in LDS when they fit the limit for their count.
-inline bool stage_in_lds(int b, int64_t nb) {
-  return act_lds_bytes(b, static_cast<uint32_t>(nb)) <= (b == 1 ? kActLdsMax : kActLdsMaxBatch);
-}
+inline bool stage_in_lds(int b, int64_t nb) { return gemv_stage_acts_in_lds(b, nb); }
 
 template <int TYPE, int B, int R, bool FUSED, bool SYNC>
 hipError_t launch_pipe(const Plan& p, hipStream_t s) {
@@ -619,55 +608,32 @@ hipError_t launch_cfg(const Plan& p, hipStream_t s) {
 }
 
 // How the activation reaches the kernel.
-enum Mode { kQuantized = 0, kLdsFused = 1, kInLaunch = 2 };
+enum Mode { kQuantized = kGemvQuantized, kLdsFused = kGemvLdsFused, kInLaunch = kGemvInLaunch };
 
-// Kernel variant per shape, from measurements on MI355X over the 7B- and
-// 70B-shaped Q4_K matrices (graphs of back-to-back launches): at batch 1 the
-// classic kernel with 4 rows per wave streams the largest matrices best
-// (6.0-6.5 TB/s; the 7B-shaped gate/up, 28672 x 4096, with the in-launch
-// handoff 13.9 against 16.5 us with 2 rows), with 2 rows per wave the
-// mid-size ones (activations staged in LDS), 1 row per wave with 2 chunks in
-// flight the small ones; at batch
-// 2-8, 8 rows per wave above 16k rows and 4 above 3k (70B layer at batch 4:
-// 142 us against 179 us with 2 rows per wave). All variants give
-// bit-identical results.
 template <int TYPE, int B, int MODE>
 hipError_t launch_b(const Plan& p, hipStream_t s) {
   constexpr bool SYNC = MODE == kInLaunch;
-  const int64_t n = p.n, k = p.nb * 32;
+  const GemvVariant v = select_gemv(TYPE, p.n, p.nb * 32, B, MODE);
+  const int ru = 10 * v.r + v.u;
   if constexpr (MODE == kLdsFused) {
-    if (n >= 8192) return launch_pipe<TYPE, B, 4, true, false>(p, s);
+    if (v.r == 4) return launch_pipe<TYPE, B, 4, true, false>(p, s);
     return launch_pipe<TYPE, B, 2, true, false>(p, s);
   } else if constexpr (B == 1) {
-    if (n >= 16384) return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
-    if (n >= 8192 && k >= 16384) return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
-    // long rows of a mid-size matrix with the in-launch handoff: two chunks
-    // per step (7B-shaped down, 4096 x 14336: 10.5 against 11.2 us; with a
-    // quantized activation one chunk stays faster, 9.7 against 10.8 us)
-    if (SYNC && n >= 3072 && n < 8192 && k >= 8192) return launch_cfg<TYPE, 1, 2, 2, SYNC>(p, s);
-    // Q4_0 / Q8_0 rows (no super-block headers, fewer instructions per
-    // block) on a quantized activation: two chunks per step (Q4_0 4096 x
-    // 14336: 8.3 against 9.0 us; 4096 x 4096: 4.2 against 4.3 us; Q8_0
-    // 14336 x 4096: 13.2-14.1 against 14.2 us in two runs; Q4_K is slower
-    // this way on the 7B-shaped q/k/v and down)
-    if (MODE == kQuantized && TYPE != kQ4_K && n >= 3072) return launch_cfg<TYPE, 1, 2, 2, SYNC>(p, s);
-    if (n >= 3072) return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
-    return launch_cfg<TYPE, 1, 1, 2, SYNC>(p, s);
-  } else {
-    // several activation rows: every row a wave owns re-uses the activation
-    // registers, and at batch 2-8 those re-reads bound the kernel, so the
-    // larger matrices take more rows per wave
-    if (n >= 16384) return launch_cfg<TYPE, B, 8, 1, SYNC>(p, s);
-    if (n >= 3072) {
-      // long rows at batch 4 and above: 8 rows per wave (70B-shaped down,
-      // 8192 x 28672: 36.8 against 37.8 us at batch 4, 48.6 against 53.2 at
-      // 8; slower at batch 2); short rows: 2 (7B-shaped q/k/v, 6144 x 4096:
-      // 9.6 against 9.7 us at batch 4, 13.6 against 14.7 at 8)
-      if (B >= 4 && k >= 16384) return launch_cfg<TYPE, B, 8, 1, SYNC>(p, s);
-      if (k <= 4096) return launch_cfg<TYPE, B, 2, 1, SYNC>(p, s);
-      return launch_cfg<TYPE, B, 4, 1, SYNC>(p, s);
+    switch (ru) {
+      case 41: return launch_cfg<TYPE, 1, 4, 1, SYNC>(p, s);
+      case 22: return launch_cfg<TYPE, 1, 2, 2, SYNC>(p, s);
+      case 21: return launch_cfg<TYPE, 1, 2, 1, SYNC>(p, s);
+      case 12: return launch_cfg<TYPE, 1, 1, 2, SYNC>(p, s);
+      default: return hipErrorInvalidValue;
     }
-    return launch_cfg<TYPE, B, 1, 1, SYNC>(p, s);
+  } else {
+    switch (ru) {
+      case 81: return launch_cfg<TYPE, B, 8, 1, SYNC>(p, s);
+      case 41: return launch_cfg<TYPE, B, 4, 1, SYNC>(p, s);
+      case 21: return launch_cfg<TYPE, B, 2, 1, SYNC>(p, s);
+      case 11: return launch_cfg<TYPE, B, 1, 1, SYNC>(p, s);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 

@@ -1,0 +1,82 @@
+// Host-side choice of the GEMV kernel instance for a product's shape. Pure
+// host C++ (no HIP device code), shared by the launchers in gemv.hip and the
+// introspection export qblk_gemv_variant.
+#include <stdio.h>
+
+#include "qblk_internal.h"
+
+namespace qblk {
+
+// Kernel variant per shape, from measurements on MI355X over the 7B- and
+// 70B-shaped Q4_K matrices (graphs of back-to-back launches): at batch 1 the
+// classic kernel with 4 rows per wave streams the largest matrices best
+// (6.0-6.5 TB/s; the 7B-shaped gate/up, 28672 x 4096, with the in-launch
+// handoff 13.9 against 16.5 us with 2 rows), with 2 rows per wave the
+// mid-size ones (activations staged in LDS), 1 row per wave with 2 chunks in
+// flight the small ones; at batch
+// 2-8, 8 rows per wave above 16k rows and 4 above 3k (70B layer at batch 4:
+// 142 us against 179 us with 2 rows per wave). All variants give
+// bit-identical results.
+GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
+  GemvVariant v{};
+  v.type = type;
+  v.b = b;
+  v.sync = mode == kGemvInLaunch;
+  v.fused = mode == kGemvLdsFused;
+  const int64_t nb = k / 32;
+  if (mode == kGemvLdsFused) {
+    v.pipe = true;
+    v.r = n >= 8192 ? 4 : 2;
+    v.u = 1;
+    v.alds = false;
+    return v;
+  }
+  v.pipe = false;
+  v.alds = gemv_stage_acts_in_lds(b, nb);
+  auto set = [&](int r, int u) {
+    v.r = r;
+    v.u = u;
+    return v;
+  };
+  if (b == 1) {
+    if (n >= 16384) return set(4, 1);
+    if (n >= 8192 && k >= 16384) return set(4, 1);
+    // long rows of a mid-size matrix with the in-launch handoff: two chunks
+    // per step (7B-shaped down, 4096 x 14336: 10.5 against 11.2 us; with a
+    // quantized activation one chunk stays faster, 9.7 against 10.8 us)
+    if (v.sync && n >= 3072 && n < 8192 && k >= 8192) return set(2, 2);
+    // Q4_0 / Q8_0 rows (no super-block headers, fewer instructions per
+    // block) on a quantized activation: two chunks per step (Q4_0 4096 x
+    // 14336: 8.3 against 9.0 us; 4096 x 4096: 4.2 against 4.3 us; Q8_0
+    // 14336 x 4096: 13.2-14.1 against 14.2 us in two runs; Q4_K is slower
+    // this way on the 7B-shaped q/k/v and down)
+    if (mode == kGemvQuantized && type != kQ4_K && n >= 3072) return set(2, 2);
+    if (n >= 3072) return set(2, 1);
+    return set(1, 2);
+  }
+  // several activation rows: every row a wave owns re-uses the activation
+  // registers, and at batch 2-8 those re-reads bound the kernel, so the
+  // larger matrices take more rows per wave
+  if (n >= 16384) return set(8, 1);
+  if (n >= 3072) {
+    // long rows at batch 4 and above: 8 rows per wave (70B-shaped down,
+    // 8192 x 28672: 36.8 against 37.8 us at batch 4, 48.6 against 53.2 at
+    // 8; slower at batch 2); short rows: 2 (7B-shaped q/k/v, 6144 x 4096:
+    // 9.6 against 9.7 us at batch 4, 13.6 against 14.7 at 8)
+    if (b >= 4 && k >= 16384) return set(8, 1);
+    if (k <= 4096) return set(2, 1);
+    return set(4, 1);
+  }
+  return set(1, 1);
+}
+
+int gemv_variant_name(const GemvVariant& v, char* buf, size_t len) {
+  const char* t = v.sync ? "true" : "false";
+  const char* a = v.alds ? "true" : "false";
+  if (v.pipe)
+    return snprintf(buf, len, "gemv_pipe_kernel<%d, %d, %d, %s, %s, %s>", v.type, v.b, v.r,
+                    v.fused ? "true" : "false", t, a);
+  return snprintf(buf, len, "gemv_kernel<%d, %d, %d, %d, %s, %s>", v.type, v.b, v.r, v.u, t, a);
+}
+
+}  // namespace qblk

@@ -74,6 +74,36 @@ inline int64_t gemv_flags_offset(int64_t batch, int64_t k) {
 inline int64_t gemv_f32_work_bytes(int64_t batch, int64_t k) {
   return gemv_flags_offset(batch, k) + 8 * 8 * gemv_flag_stride(k);
 }
+// GEMV activation staging: a workgroup copies the activation rows into LDS,
+// per row whole 2 KiB chunks (64 blocks of 32 codes), then the (d, sum)
+// pairs of all rows. Staged when the copy fits 16 KiB for one activation row
+// (70B-shaped down, 36 KiB: 26.9 us staged against 24.6 us read from L2) or
+// 40 KiB for several (70B-shaped gate/up at batch 4: 59.8 against 62.1 us).
+constexpr uint32_t act_lds_row(uint32_t nb) { return ((nb + 63u) >> 6) * 2048u; }
+constexpr uint32_t act_lds_bytes(int b, uint32_t nb) {
+  return static_cast<uint32_t>(b) * (act_lds_row(nb) + 8u * nb);
+}
+constexpr uint32_t kActLdsMax = 16384;
+constexpr uint32_t kActLdsMaxBatch = 40960;
+constexpr bool gemv_stage_acts_in_lds(int b, int64_t nb) {
+  return act_lds_bytes(b, static_cast<uint32_t>(nb)) <= (b == 1 ? kActLdsMax : kActLdsMaxBatch);
+}
+// Which GEMV kernel instance a product runs (pure host logic, no GPU):
+// gemv_kernel<type, b, r, u, sync, alds> or gemv_pipe_kernel<type, b, r,
+// fused, sync, alds>. mode: how the activation reaches the kernel.
+enum : int { kGemvQuantized = 0, kGemvLdsFused = 1, kGemvInLaunch = 2 };
+struct GemvVariant {
+  int type;
+  int b;      // activation rows of the launch (1..8)
+  int r;      // weight rows per wave
+  int u;      // chunks per step (classic kernel)
+  bool pipe;  // gemv_pipe_kernel (else gemv_kernel)
+  bool sync;  // activation quantized once per launch (in-launch handoff)
+  bool alds;  // activation rows staged in LDS
+  bool fused; // activation quantized in every workgroup's LDS
+};
+GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode);
+int gemv_variant_name(const GemvVariant& v, char* buf, size_t len);
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
                            int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
                            hipStream_t s);

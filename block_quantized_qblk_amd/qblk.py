@@ -29,10 +29,9 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        # build once from source; a failure here is an error, there is no
-        # fallback path
-        from . import build_lib
-        build_lib.build()
+        # there is no fallback path: the library must have been built
+        raise RuntimeError(f"{LIB_PATH} is missing; build it first with "
+                           "`python -m block_quantized_qblk_amd.build_lib`")
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     sig = {
@@ -51,6 +50,7 @@ def _load():
         "qblk_gemv_f32": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp, vp]),
         "qblk_gemv_float": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]),
         "qblk_gemv_multi": (i32, [i32, vp, i32, i64, vp]),
+        "qblk_gemv_variant": (i32, [i32, i64, i64, i64, i32, ctypes.c_char_p, ctypes.c_size_t]),
         "qblk_kv_cache_bytes": (ctypes.c_size_t, [i32, i64, i64, i64]),
         "qblk_kv_store": (i32, [i32, vp, i64, i64, i64, vp, i64, i64, vp]),
         "qblk_kv_scores": (i32, [i32, vp, i64, i64, i64, i64, vp, i64, vp, i64, vp]),
@@ -226,6 +226,15 @@ class GemvDesc(ctypes.Structure):
     """One product of qblk_gemv_multi (mirrors qblk_gemv_desc)."""
     _fields_ = [("wq", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("xq", ctypes.c_void_p), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
+def qblk_gemv_variant(wtype, n, k, batch=1, fused=False):
+    """Name of the kernel instance qblk_gemv (fused=False) or qblk_gemv_f32
+    (fused=True) launches for this shape (host only, no GPU)."""
+    buf = ctypes.create_string_buffer(128)
+    _check(_load().qblk_gemv_variant(_type(wtype), int(n), int(k), int(batch), int(bool(fused)),
+                                     buf, len(buf)), "qblk_gemv_variant")
+    return buf.value.decode()
 
 
 def qblk_gemv_multi(wtype, products, batch, stream=None):

@@ -22,7 +22,9 @@
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without waiting. Calls are reentrant and thread-safe.
  *   - Every argument is validated BEFORE anything is enqueued; on any error
- *     nothing is enqueued and a negative qblk_status is returned.
+ *     nothing is enqueued and a negative qblk_status is returned (0 =
+ *     success, negative = failure, the convention of the decode call on the
+ *     page "【AI】端侧模型部署llama.cpp篇", section llama_decode).
  *   - Sizes are element counts (int64_t). m, n or batch equal to 0 is a valid
  *     empty call that enqueues nothing and returns QBLK_OK. Negative sizes are
  *     QBLK_ERR_ARG.
@@ -66,7 +68,16 @@
 extern "C" {
 #endif
 
-#define QBLK_ABI_VERSION 1
+/* ABI version: the entry points and their argument lists. Layout version:
+ * the byte layouts above (packed weight rows, activation buffer, KV cache
+ * rows), which the library fixes itself where the pages list only fields
+ * ("llama.cpp 推理引擎", §5.3-§5.5). qblk_abi_version() returns both, as
+ * QBLK_VERSION; a caller holding packed buffers checks the layout part. */
+#define QBLK_ABI_VERSION 2
+#define QBLK_LAYOUT_VERSION 1
+#define QBLK_VERSION ((QBLK_ABI_VERSION << 8) | QBLK_LAYOUT_VERSION)
+#define QBLK_VERSION_ABI(v) ((v) >> 8)
+#define QBLK_VERSION_LAYOUT(v) ((v) & 0xFF)
 
 typedef enum {
   QBLK_Q4_0 = 1, /* 32-blocks, 4-bit codes, fp32 scale: 20 B / 32 weights */
@@ -91,7 +102,7 @@ typedef enum {
 
 #define QBLK_GEMV_MAX_BATCH 64
 
-/* Returns QBLK_ABI_VERSION of the loaded library. */
+/* QBLK_VERSION of the loaded library: (ABI version << 8) | layout version. */
 int qblk_abi_version(void);
 
 /* Human-readable text for a qblk_status value (static storage). */
@@ -132,7 +143,7 @@ size_t qblk_act_bytes(int64_t m, int64_t k);
  * Errors: QBLK_ERR_ARG (null, negative n, unknown type), QBLK_ERR_SHAPE
  * (k invalid, ldw < k), QBLK_ERR_ALIGN, QBLK_ERR_LAUNCH.
  */
-int qblk_pack_weights(int type, const float *w, int64_t n, int64_t k,
+qblk_status qblk_pack_weights(int type, const float *w, int64_t n, int64_t k,
                       int64_t ldw, void *wq, hipStream_t stream);
 
 /*
@@ -145,11 +156,15 @@ int qblk_pack_weights(int type, const float *w, int64_t n, int64_t k,
  * Errors: QBLK_ERR_ARG, QBLK_ERR_SHAPE (k % 32 != 0, k <= 0, ldx < k),
  * QBLK_ERR_ALIGN, QBLK_ERR_LAUNCH.
  */
-int qblk_quantize_act(const float *x, int64_t m, int64_t k, int64_t ldx,
+qblk_status qblk_quantize_act(const float *x, int64_t m, int64_t k, int64_t ldx,
                       void *xq, hipStream_t stream);
 
 /*
- * Decode-path product (few activation rows): for b < batch, n < n:
+ * Decode-path product (few activation rows). The per-block integer dot with
+ * the scales applied outside it is the pages' quantized dot kernel
+ * ("llama.cpp 推理引擎", §6.4 ggml_vec_dot_q4_0; wmrh.cn "bare engine"
+ * article, §2.2: the Q4_K x Q8 dot as int4 x int8 multiply-adds); Q4_K
+ * scale and min per sub-block as in §5.5. For b < batch, n < n:
  *   y[b*ldy + n] = sum over 32-blocks j of
  *     Q4_0/Q8_0: dw[n][j] * dx[b][j] * S[b][n][j]
  *     Q4_K     : dx[b][j] * ((d*sc_j)[n] * S[b][n][j] + (d_min*mn_j)[n] * A[b][j])
@@ -162,7 +177,7 @@ int qblk_quantize_act(const float *x, int64_t m, int64_t k, int64_t ldx,
  * QBLK_ERR_ALIGN, QBLK_ERR_UNSUPPORTED (batch > QBLK_GEMV_MAX_BATCH),
  * QBLK_ERR_LAUNCH.
  */
-int qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void *xq,
+qblk_status qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void *xq,
               int64_t batch, float *y, int64_t ldy, hipStream_t stream);
 
 /*
@@ -188,7 +203,7 @@ typedef struct qblk_gemv_desc {
   float *y;
   int64_t ldy;
 } qblk_gemv_desc;
-int qblk_gemv_multi(int type, const qblk_gemv_desc *descs, int count, int64_t batch,
+qblk_status qblk_gemv_multi(int type, const qblk_gemv_desc *descs, int count, int64_t batch,
                     hipStream_t stream);
 
 /*
@@ -219,9 +234,26 @@ int qblk_gemv_multi(int type, const qblk_gemv_desc *descs, int count, int64_t ba
  */
 int qblk_gemv_f32_max_batch(int64_t k);
 size_t qblk_gemv_f32_work_bytes(int64_t batch, int64_t k); /* 0 if invalid */
-int qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const float *x,
+qblk_status qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const float *x,
                   int64_t ldx, int64_t batch, float *y, int64_t ldy, void *work,
                   hipStream_t stream);
+
+/*
+ * Introspection (host only, no GPU work): the name of the kernel instance
+ * that qblk_gemv (fused == 0) or qblk_gemv_f32 (fused != 0) launches for
+ * this shape, for the first group of up to 8 activation rows, as the
+ * kernel's template arguments: "gemv_kernel<type, rows, rows per wave,
+ * chunks per step, in-launch quantization, activations in LDS>" or
+ * "gemv_pipe_kernel<type, rows, rows per wave, per-workgroup quantization,
+ * in-launch quantization, activations in LDS>". Written NUL-terminated into
+ * name[len]. Lets a test check that the instances a workload runs are the
+ * ones its parity cases cover.
+ * Errors: QBLK_ERR_ARG (type, n <= 0, batch <= 0, null name, len too
+ * small), QBLK_ERR_SHAPE (k invalid), QBLK_ERR_UNSUPPORTED (batch beyond
+ * the entry point's limit).
+ */
+qblk_status qblk_gemv_variant(int type, int64_t n, int64_t k, int64_t batch, int fused, char *name,
+                      size_t len);
 
 /*
  * Decode-path product with fp32 activations and no activation quantization,
@@ -238,17 +270,21 @@ int qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const float *x
  * Errors: as qblk_gemv, plus QBLK_ERR_SHAPE for ldx < k and QBLK_ERR_ALIGN
  * for x or ldx.
  */
-int qblk_gemv_float(int type, const void *wq, int64_t n, int64_t k, const float *x,
+qblk_status qblk_gemv_float(int type, const void *wq, int64_t n, int64_t k, const float *x,
                     int64_t ldx, int64_t batch, float *y, int64_t ldy,
                     hipStream_t stream);
 
 /*
  * Prefill-path product: the same result as qblk_gemv for m activation rows,
  * Y[m][ldy] = X * W^T, computed with int8 matrix-core tiles. Any m >= 0.
+ * Per block the same integer dot and outside scales as qblk_gemv
+ * ("llama.cpp 推理引擎", §6.4; wmrh.cn "bare engine" article, §2.2); prefill
+ * processes many tokens at once and is compute-bound ("llama.cpp 推理引擎",
+ * §7.3), hence the matrix cores.
  * Errors as qblk_gemv (no batch limit), plus QBLK_ERR_UNSUPPORTED for
  * k > 2^24.
  */
-int qblk_gemm(int type, const void *wq, int64_t n, int64_t k, const void *xq,
+qblk_status qblk_gemm(int type, const void *wq, int64_t n, int64_t k, const void *xq,
               int64_t m, float *y, int64_t ldy, hipStream_t stream);
 
 /*
@@ -273,7 +309,7 @@ size_t qblk_kv_cache_bytes(int type, int64_t n_kv, int64_t n_ctx, int64_t head_d
  * (head_dim, n_ctx <= 0, pos outside [0, n_ctx), ldx < head_dim),
  * QBLK_ERR_ALIGN, QBLK_ERR_UNSUPPORTED (n_kv > 65535), QBLK_ERR_LAUNCH.
  */
-int qblk_kv_store(int type, const float *x, int64_t n_kv, int64_t head_dim, int64_t ldx,
+qblk_status qblk_kv_store(int type, const float *x, int64_t n_kv, int64_t head_dim, int64_t ldx,
                   void *cache, int64_t n_ctx, int64_t pos, hipStream_t stream);
 
 /*
@@ -290,17 +326,20 @@ int qblk_kv_store(int type, const float *x, int64_t n_kv, int64_t head_dim, int6
  * lds < n_tok), QBLK_ERR_ALIGN (cache, q: 16 bytes; scores: 4),
  * QBLK_ERR_UNSUPPORTED (n_head / n_kv > 8, n_kv > 65535), QBLK_ERR_LAUNCH.
  */
-int qblk_kv_scores(int type, const void *cache, int64_t n_kv, int64_t n_ctx, int64_t n_tok,
+qblk_status qblk_kv_scores(int type, const void *cache, int64_t n_kv, int64_t n_ctx, int64_t n_tok,
                    int64_t head_dim, const void *q, int64_t n_head, float *scores, int64_t lds,
                    hipStream_t stream);
 
 /*
  * Test export: the integer block sums S[mm][nn][j] (int32, layout
  * [m][n][k/32]) that qblk_gemv / qblk_gemm scale and accumulate, computed
- * with the same device unpack and dot code. Intended for small shapes.
+ * with the same device unpack and dot code: the integer part of the pages'
+ * block dot, before any scale ("llama.cpp 推理引擎", §6.4: nibble - 8 times
+ * the activation; wmrh.cn "bare engine" article, §2.2: int4 x int8
+ * multiply-adds summed to int32). Intended for small shapes.
  * Errors as qblk_gemv (no batch limit).
  */
-int qblk_block_sums(int type, const void *wq, int64_t n, int64_t k,
+qblk_status qblk_block_sums(int type, const void *wq, int64_t n, int64_t k,
                     const void *xq, int64_t m, int32_t *sums,
                     hipStream_t stream);
 

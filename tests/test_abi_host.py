@@ -32,7 +32,11 @@ def _declared():
 
 def test_library_loads_and_reports_abi():
     lib = qblk.lib()
-    assert lib.qblk_abi_version() == 1
+    text = open(HEADER).read()
+    abi = int(re.search(r"#define QBLK_ABI_VERSION (\d+)", text).group(1))
+    layout = int(re.search(r"#define QBLK_LAYOUT_VERSION (\d+)", text).group(1))
+    v = lib.qblk_abi_version()
+    assert (v >> 8, v & 0xFF) == (abi, layout) == (2, 1)
     assert qblk.strerror(0) == "ok"
     assert "shape" in qblk.strerror(-2)
 
@@ -225,3 +229,40 @@ def test_gemv_multi_validation():
     assert f(3, ctypes.cast(bad, ctypes.c_void_p), 2, 1, NULL) == ERR_ALIGN
     bad = (D * 2)(good, D(FAKE, 16, 256, FAKE, FAKE, 15))     # ldy < n
     assert f(3, ctypes.cast(bad, ctypes.c_void_p), 2, 1, NULL) == ERR_SHAPE
+
+
+def test_gemv_variant_names():
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 1, True) == \
+        "gemv_kernel<3, 1, 4, 1, true, true>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 4, True) == \
+        "gemv_kernel<3, 4, 8, 1, true, true>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 1024, 2048, 1, True).startswith("gemv_pipe_kernel<3, 1, 2, true")
+    assert qblk.qblk_gemv_variant(o.TYPE_Q8_0, 14336, 4096, 1, False) == \
+        "gemv_kernel<2, 1, 2, 2, false, true>"
+    lib = qblk.lib()
+    buf = ctypes.create_string_buffer(8)
+    assert lib.qblk_gemv_variant(3, 57344, 8192, 1, 1, buf, 8) == ERR_ARG      # too short
+    assert lib.qblk_gemv_variant(3, 57344, 8100, 1, 1, buf, 8) == ERR_SHAPE
+    assert lib.qblk_gemv_variant(3, 57344, 8192, 9, 1, buf, 8) == ERR_UNSUPPORTED
+    assert lib.qblk_gemv_variant(9, 57344, 8192, 1, 1, buf, 8) == ERR_ARG
+
+
+def test_benchmarked_gemv_instances_have_parity_cases():
+    """Every GEMV kernel instance the benchmark times (the host's kernel
+    selection replayed for each of its launches) is run by at least one GPU
+    parity case."""
+    import bench
+    from block_quantized_qblk_amd import synth
+    from tests import gemv_cases
+
+    def name(case):
+        t, n, k, b, fused = case
+        return qblk.qblk_gemv_variant(t, n, k, min(b, 8), fused)
+
+    covered = {name(c) for c in gemv_cases.covered()}
+    missing = {}
+    for c in bench.gemv_launches(synth):
+        v = name(c)
+        if v not in covered:
+            missing[c] = v
+    assert not missing, missing

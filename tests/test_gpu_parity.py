@@ -7,6 +7,7 @@ import pytest
 
 from block_quantized_qblk_amd import qblk, synth
 from oracle import qblk_oracle as o
+from tests import gemv_cases as cases
 from tests.gpu_util import (REL_TOL, check_rel, dev, dev_pack, dev_quantize, expected, host,
                             oracle_act, torch)
 
@@ -182,7 +183,7 @@ def _exact_case(wtype, n, k, m, seed):
 
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("batch", [1, 3, 8, 11])
+@pytest.mark.parametrize("batch", cases.GEMV_EXACT_BATCH)
 def test_gemv_exact_arithmetic(wtype, batch):
     print(f"gemv exact {TNAME[wtype]} batch={batch}", flush=True)
     n, k = 67, 2304 if wtype == o.TYPE_Q4_K else 2336
@@ -204,9 +205,7 @@ def test_gemm_exact_arithmetic(wtype, m):
 # ================================================================ random products
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("n,k,batch", [(37, 1024, 1), (300, 4096, 1), (129, 2304, 4),
-                                       (64, 256, 8), (70, 512, 64), (3100, 512, 2),
-                                       (16400, 512, 5)])
+@pytest.mark.parametrize("n,k,batch", cases.GEMV_RANDOM)
 def test_gemv_random(wtype, n, k, batch):
     print(f"gemv {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
     rng = np.random.default_rng(31 * wtype + n + batch)
@@ -285,14 +284,7 @@ def _full_size_check(wtype, w_dev, x_np, rows, use_gemm=False):
     return check_rel(y[:, rows], expected(wtype, w_rows, x_np))
 
 
-@pytest.mark.parametrize("case", [
-    ("Q4_0 4096x4096", 1, o.TYPE_Q4_0, 4096, 4096),
-    ("Q8_0 14336x4096", 2, o.TYPE_Q8_0, 14336, 4096),
-    ("Q4_K q 4096x4096", 3, o.TYPE_Q4_K, 4096, 4096),
-    ("Q4_K k 1024x4096", 3, o.TYPE_Q4_K, 1024, 4096),
-    ("Q4_K gate 14336x4096", 3, o.TYPE_Q4_K, 14336, 4096),
-    ("Q4_K down 4096x14336", 3, o.TYPE_Q4_K, 4096, 14336),
-])
+@pytest.mark.parametrize("case", cases.GEMV_FULL_SIZE)
 def test_gemv_full_size_sampled(case):
     name, wl, wtype, n, k = case
     print(f"full-size gemv {name}", flush=True)
@@ -301,9 +293,8 @@ def test_gemv_full_size_sampled(case):
     _full_size_check(wtype, dev(w), x, _sample_rows(n, 96, n + k))
 
 
-@pytest.mark.parametrize("m", [1, 4])
-@pytest.mark.parametrize("name,n,k", [("q", 8192, 8192), ("gate", 28672, 8192),
-                                      ("down", 8192, 28672)])
+@pytest.mark.parametrize("m", cases.GEMV_70B_BATCH)
+@pytest.mark.parametrize("name,n,k", cases.GEMV_70B)
 def test_gemv_70b_layer_sampled(name, n, k, m):
     print(f"70B-shaped gemv {name} {n}x{k} batch={m}", flush=True)
     w = synth.torch_weights("student_t", 5000 + n % 97, n, k)
@@ -313,7 +304,7 @@ def test_gemv_70b_layer_sampled(name, n, k, m):
     torch().cuda.empty_cache()
 
 
-@pytest.mark.parametrize("m", [512, 1, 8, 64])
+@pytest.mark.parametrize("m", cases.GEMM_PREFILL_M)
 def test_gemm_prefill_full_size_sampled(m):
     print(f"full-size gemm Q4_K m={m}", flush=True)
     n, k = 14336, 4096
@@ -327,11 +318,7 @@ def test_gemm_prefill_full_size_sampled(m):
 # ================================================================ fused quantize + GEMV
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("n,k,batch", [(37, 1024, 1), (300, 4096, 3), (4100, 2304, 1),
-                                       (9000, 8192, 1), (129, 4096, 6), (70, 256, 8),
-                                       (2000, 28672, 1), (17000, 4096, 1), (8200, 16384, 1),
-                                       (16400, 4096, 3), (16384, 2048, 8),
-                                       (5000, 28672, 4)])
+@pytest.mark.parametrize("n,k,batch", cases.GEMV_F32)
 def test_gemv_f32_matches_quantize_then_gemv(wtype, n, k, batch):
     if wtype == o.TYPE_Q4_K and k % 256:
         pytest.skip("Q4_K needs k % 256 == 0")
@@ -358,10 +345,7 @@ def _in_launch(n, k, batch):
 
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("n,k,batch", [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1),
-                                       (4096, 14336, 1), (4096, 4096, 1), (1024, 4096, 2),
-                                       (9000, 4096, 4), (16400, 2304, 3), (3, 1 << 24, 1),
-                                       (3, 1 << 24, 4)])
+@pytest.mark.parametrize("n,k,batch", cases.GEMV_F32_IN_LAUNCH)
 def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
     """Products that quantize the activation once per launch into the
     workspace, one slice per (activation row, 64 blocks). One
@@ -388,6 +372,29 @@ def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
     if k <= 28672:
         rows = _sample_rows(n, 16, n)
         check_rel(fused[:, rows], expected(wtype, w[rows], x))
+
+
+@pytest.mark.parametrize("batch", cases.GEMV_F32_70B_BATCH)
+@pytest.mark.parametrize("name,n,k", cases.GEMV_F32_70B)
+def test_gemv_f32_70b_decode_shapes_sampled(name, n, k, batch):
+    """qblk_gemv_f32 on the matrices of the 70B-shaped decode token as the
+    benchmark launches them (q/k/v and gate/up concatenated by rows):
+    bitwise equal to quantize + qblk_gemv, and within the tolerance of the
+    oracle on sampled rows."""
+    print(f"gemv_f32 70B-shaped {name} {n}x{k} batch={batch}", flush=True)
+    t = torch()
+    w = synth.torch_weights("student_t", 5100 + n % 89, n, k)
+    x = synth.act(5, batch, k)
+    wq = qblk.qblk_pack_weights(o.TYPE_Q4_K, w)
+    xd = dev(x)
+    fused = host(qblk.qblk_gemv_f32(o.TYPE_Q4_K, wq, n, k, xd))
+    two_step = host(qblk.qblk_gemv(o.TYPE_Q4_K, wq, n, k, qblk.qblk_quantize_act(xd), batch))
+    assert np.array_equal(fused.view(np.uint32), two_step.view(np.uint32))
+    rows = _sample_rows(n, 40, n + batch)
+    w_rows = host(w[t.from_numpy(rows).cuda()])
+    del w, wq
+    t.cuda.empty_cache()
+    check_rel(fused[:, rows], expected(o.TYPE_Q4_K, w_rows, x))
 
 
 def test_gemv_f32_strided_rows_and_limits():
