@@ -87,6 +87,101 @@ def time_replays(torch, graphs, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+class ClockSampler:
+    """Samples the GPU engine clock (MHz) from a background thread while a
+    timed region runs: the card's sysfs pp_dpm_sclk (the active level), else
+    `amd-smi metric --clock --json`. summary() is None when neither source
+    answers."""
+
+    def __init__(self, dev_index=0, period=0.05):
+        self.dev_index, self.period = dev_index, period
+        self.samples, self.source = [], None
+        self._stop = None
+
+    def _sysfs_path(self):
+        import glob
+        try:
+            import torch
+            props = torch.cuda.get_device_properties(self.dev_index)
+            bus = "%04x:%02x:%02x" % (getattr(props, "pci_domain_id", 0), props.pci_bus_id,
+                                      props.pci_device_id)
+            cands = glob.glob(f"/sys/bus/pci/devices/{bus}*/pp_dpm_sclk")
+            if cands:
+                return cands[0]
+        except Exception:
+            pass
+        cands = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        return cands[0] if len(cands) == 1 else None
+
+    @staticmethod
+    def _read_sysfs(path):
+        import re
+        for line in open(path).read().splitlines():
+            if line.rstrip().endswith("*"):
+                m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                if m:
+                    return float(m.group(1))
+        return None
+
+    def _read_amdsmi(self):
+        import re
+        import subprocess
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json", "-g", str(self.dev_index)],
+                           capture_output=True, text=True, timeout=10)
+        if r.returncode != 0:
+            return None
+        text = r.stdout
+        i = text.find("gfx")
+        if i < 0:
+            i = text.find("GFX")
+        m = re.search(r'"clk"\s*:\s*\{?\s*"value"\s*:\s*"?(\d+)', text[i:]) if i >= 0 else None
+        return float(m.group(1)) if m else None
+
+    def _sample(self):
+        path = self._sysfs_path()
+        reader = None
+        if path:
+            try:
+                if self._read_sysfs(path) is not None:
+                    reader, self.source = (lambda: self._read_sysfs(path)), path
+            except OSError:
+                pass
+        if reader is None:
+            try:
+                if self._read_amdsmi() is not None:
+                    reader, self.source = self._read_amdsmi, "amd-smi metric --clock"
+            except Exception:
+                pass
+        if reader is None:
+            return
+        while not self._stop.wait(self.period):
+            try:
+                v = reader()
+            except Exception:
+                v = None
+            if v is not None:
+                self.samples.append(v)
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._sample, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        s = sorted(self.samples)
+        return {"min": s[0], "median": s[len(s) // 2], "max": s[-1], "samples": len(s),
+                "source": self.source}
+
+
 # ---------------------------------------------------------------- decode model
 
 class DecodeModel:
@@ -175,6 +270,12 @@ class DecodeModel:
                 raise RuntimeError(f"graph replay differs from the eager run ({g})")
         return graph
 
+    def fallbacks(self):
+        """Handoff fallbacks counted in this model's workspaces (zeroed when
+        they were allocated)."""
+        return sum(self.qblk.handoff_fallbacks(self.work[g], self.batch, k)
+                   for g, _, _, k in self.groups)
+
     def kernel_times(self, layers):
         """Per-launch GEMV time: for each group, one HIP graph of its product
         over `layers` layers back to back, bracketed by HIP events on the
@@ -246,7 +347,8 @@ def main():
     m1 = DecodeModel(torch, qblk, synth, synth.LAYER_70B, args.layers, 5000, "student_t", 1, dev)
     log(f"packed {m1.weight_bytes / 1e9:.2f} GB in {time.time() - t0:.1f}s")
     g1 = m1.capture()
-    ms_tok = time_replays(torch, [g1], args.steps, args.warmup)
+    with ClockSampler(dev_index=0) as clocks:
+        ms_tok = time_replays(torch, [g1], args.steps, args.warmup)
     value = m1.weight_bytes / (ms_tok * 1e-3) / 1e9
     log(f"batch 1: {ms_tok:.3f} ms/token, {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% "
         f"of HBM peak)")
@@ -272,9 +374,12 @@ def main():
     log(f"batch 1, quantize + GEMV launches: {ms_two:.3f} ms/token; GEMV alone {per_two}")
     m1.two_step = False
 
+    fallbacks = m1.fallbacks()
     m1.set_batch(4, 5950)
     g4 = m1.capture()
     ms_tok4 = time_replays(torch, [g4], max(5, args.steps // 3), 1)
+    fallbacks += m1.fallbacks()
+    log(f"handoff fallbacks over every fused launch: {fallbacks}")
     log(f"batch 4: {ms_tok4:.3f} ms/step, {m1.weight_bytes / (ms_tok4 * 1e-3) / 1e9:.1f} GB/s")
     del g4, m1
     torch.cuda.empty_cache()
@@ -323,6 +428,8 @@ def main():
             "two_step_ms_per_step": round(ms_two, 6),
             "two_step_GBps": round(m_bytes(qblk, synth, args.layers) / (ms_two * 1e-3) / 1e9, 2),
             "two_step_gemv_per_launch": per_two,
+            "handoff_fallbacks": fallbacks,
+            "engine_clock_mhz": clocks.summary(),
         },
         "roofline": {
             "bound": "hbm",
@@ -508,6 +615,7 @@ def gemm_bench(torch, qblk, synth, dev, iters, copies=16):
         wqs.append(qblk.qblk_pack_weights(Q4_K, w))
         del w
     res = {}
+    gemm_clock = None
     for m in (512, 1, 8, 64):
         x = synth.torch_activations(4099, m, k, device=dev)
         xq = qblk.qblk_quantize_act(x)
@@ -517,8 +625,11 @@ def gemm_bench(torch, qblk, synth, dev, iters, copies=16):
         if m <= 64:
             fns.append(("gemv", qblk.qblk_gemv))
         for fname, f in fns:
-            us = graph_launches(torch, lambda i: f(Q4_K, wqs[i % copies], n, k, xq, m, y=y),
-                                launches=iters, warm_s=0.1)
+            with ClockSampler(dev_index=0) as clk:
+                us = graph_launches(torch, lambda i: f(Q4_K, wqs[i % copies], n, k, xq, m, y=y),
+                                    launches=iters, warm_s=0.1)
+            if m == 512:
+                gemm_clock = clk.summary()
             ops = 2.0 * m * n * k
             row[fname] = {"us": round(us, 3), "TOPS": round(ops / (us * 1e-6) / 1e12, 2),
                           "weight_GBps": round(qblk.qblk_weight_bytes(Q4_K, n, k)
@@ -532,6 +643,7 @@ def gemm_bench(torch, qblk, synth, dev, iters, copies=16):
         "workload": "q4_k_gemm_512x14336x4096",
         "TOPS": g["TOPS"],
         "us": g["us"],
+        "engine_clock_mhz": gemm_clock,
         "roofline": {"bound": "mfma", "kernel": "gemm_kernel<3>", "achieved": g["TOPS"],
                      "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                      "frac": round(g["TOPS"] / INT8_PEAK_TOPS, 4),

@@ -11,6 +11,9 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+// the in-launch handoff's wait bound for launches from this thread (a test
+// setting; qblk_gemv_f32_set_wait_limit)
+thread_local int64_t g_wait_ticks = qblk::kGemvWaitTicks;
 
 bool valid_type(int t) {
   return t == QBLK_Q4_0 || t == QBLK_Q8_0 || t == QBLK_Q4_K || t == QBLK_Q4_0_F16;
@@ -144,7 +147,17 @@ QBLK_EXPORT qblk_status qblk_gemv_f32(int type, const void* wq, int64_t n, int64
   if (batch > qblk::gemv_f32_max_batch(k)) return QBLK_ERR_UNSUPPORTED;
   if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
-  return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, work, stream));
+  return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, work, g_wait_ticks, stream));
+}
+
+QBLK_EXPORT size_t qblk_gemv_f32_fallback_offset(int64_t batch, int64_t k) {
+  if (qblk_gemv_f32_work_bytes(batch, k) == 0 || batch == 0) return 0;
+  return static_cast<size_t>(qblk::gemv_fallback_offset(batch, k));
+}
+
+QBLK_EXPORT qblk_status qblk_gemv_f32_set_wait_limit(int64_t ticks) {
+  g_wait_ticks = ticks < 0 ? qblk::kGemvWaitTicks : ticks;
+  return QBLK_OK;
 }
 
 QBLK_EXPORT qblk_status qblk_gemv_variant(int type, int64_t n, int64_t k, int64_t batch, int fused,

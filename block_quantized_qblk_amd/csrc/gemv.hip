@@ -88,6 +88,8 @@ struct GemvArgs {
   uint64_t* flags;     // [8][flag_stride] u64
   uint32_t nslices;    // ceil(nb / 64) slices per activation row
   uint32_t flag_stride;
+  uint32_t* fallbacks; // counter of workgroups that gave up waiting
+  uint64_t wait_ticks; // the wait bound, 100 MHz ticks
 };
 
 // ---------------------------------------------------------------- in-kernel handoff
@@ -155,7 +157,8 @@ __device__ __forceinline__ void produce(const GemvArgs& g, uint64_t tag) {
 // relaxed load per slice, spread over its threads) until every slice carries
 // this launch's tag. Activation codes are read only after that, so no cache
 // holds a line of them from before this launch (the kernel start invalidated
-// the caches). The wait is bounded: after about 20 ms the workgroup
+// the caches). The wait is bounded (20 ms unless a test lowers it): past the
+// bound the workgroup counts itself in the workspace's fallback counter and
 // quantizes every slice itself (the same bytes the producers write), so the
 // kernel finishes with the right result even if the producers were never
 // scheduled. All exits are decided by workgroup-wide reductions.
@@ -168,9 +171,11 @@ __device__ __forceinline__ void wait_slices(const GemvArgs& g, uint64_t tag) {
     for (uint32_t sl = threadIdx.x; sl < B * g.nslices; sl += 256u)
       pending |= __hip_atomic_load(f + sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag;
     if (!__syncthreads_or(pending)) return;
-    const int late = __builtin_amdgcn_s_memrealtime() - t0 > 2000000ull;  // 100 MHz clock
+    const int late = __builtin_amdgcn_s_memrealtime() - t0 > g.wait_ticks;  // 100 MHz clock
     if (__syncthreads_or(late)) break;
   }
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(g.fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (uint32_t sl = 0; sl < B * g.nslices; ++sl) quantize_slice(g, sl);
   __threadfence();
   __syncthreads();
@@ -546,8 +551,10 @@ struct Plan {
   int64_t ldy;
   const float* x;     // fp32 activations (fused variants)
   int64_t ldx;
-  uint8_t* work;      // SYNC: workspace (activation buffer, then flags)
+  uint8_t* work;      // SYNC: workspace (activation buffer, flags, fallback counter)
   int64_t flags_off;
+  int64_t fallback_off;
+  int64_t wait_ticks;
 };
 
 inline GemvArgs make_args(const Plan& p) {
@@ -568,6 +575,8 @@ inline GemvArgs make_args(const Plan& p) {
   g.flags = p.work ? reinterpret_cast<uint64_t*>(p.work + p.flags_off) : nullptr;
   g.nslices = static_cast<uint32_t>((p.nb + 63) / 64);
   g.flag_stride = static_cast<uint32_t>(gemv_flag_stride(p.nb * 32));
+  g.fallbacks = p.work ? reinterpret_cast<uint32_t*>(p.work + p.fallback_off) : nullptr;
+  g.wait_ticks = static_cast<uint64_t>(p.wait_ticks);
   return g;
 }
 
@@ -774,7 +783,7 @@ hipError_t launch_gemv_multi(int type, const GemvDesc* d, int count, int64_t bat
 // quantization in every workgroup would cost more than the weight stream).
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
                            int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
-                           hipStream_t s) {
+                           int64_t wait_ticks, hipStream_t s) {
   Plan p{};
   p.W.base = static_cast<const uint8_t*>(wq);
   p.W.row_bytes = row_bytes(type, k);
@@ -793,6 +802,8 @@ hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const
   p.A = make_act(work, batch, k);
   p.work = static_cast<uint8_t*>(work);
   p.flags_off = gemv_flags_offset(batch, k);
+  p.fallback_off = gemv_fallback_offset(batch, k);
+  p.wait_ticks = wait_ticks;
   return launch_type<kInLaunch>(type, bc, p, s);
 }
 

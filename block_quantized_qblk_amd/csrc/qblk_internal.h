@@ -71,9 +71,15 @@ inline int64_t gemv_flag_stride(int64_t k) {  // one flag per (activation row, 6
 inline int64_t gemv_flags_offset(int64_t batch, int64_t k) {
   return (batch * k + 8 * batch * (k / 32) + 255) / 256 * 256;
 }
-inline int64_t gemv_f32_work_bytes(int64_t batch, int64_t k) {
+// then one uint32 counter of handoff fallbacks (workgroups that stopped
+// waiting for the producers and quantized the activation themselves), on a
+// 256-byte line of its own
+inline int64_t gemv_fallback_offset(int64_t batch, int64_t k) {
   return gemv_flags_offset(batch, k) + 8 * 8 * gemv_flag_stride(k);
 }
+inline int64_t gemv_f32_work_bytes(int64_t batch, int64_t k) { return gemv_fallback_offset(batch, k) + 256; }
+// The handoff's bounded wait, in ticks of the 100 MHz realtime counter: 20 ms.
+constexpr int64_t kGemvWaitTicks = 2000000;
 // GEMV activation staging: a workgroup copies the activation rows into LDS,
 // per row whole 2 KiB chunks (64 blocks of 32 codes), then the (d, sum)
 // pairs of all rows. Staged when the copy fits 16 KiB for one activation row
@@ -104,9 +110,10 @@ struct GemvVariant {
 };
 GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode);
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len);
+// wait_ticks: the handoff's wait bound (kGemvWaitTicks outside tests)
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
                            int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
-                           hipStream_t s);
+                           int64_t wait_ticks, hipStream_t s);
 // one product of a multi-product GEMV launch (quantized activations)
 struct GemvDesc {
   const void* wq;

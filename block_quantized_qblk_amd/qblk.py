@@ -48,6 +48,8 @@ def _load():
         "qblk_gemv_f32_max_batch": (i32, [i64]),
         "qblk_gemv_f32_work_bytes": (ctypes.c_size_t, [i64, i64]),
         "qblk_gemv_f32": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp, vp]),
+        "qblk_gemv_f32_fallback_offset": (ctypes.c_size_t, [i64, i64]),
+        "qblk_gemv_f32_set_wait_limit": (i32, [i64]),
         "qblk_gemv_float": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]),
         "qblk_gemv_multi": (i32, [i32, vp, i32, i64, vp]),
         "qblk_gemv_variant": (i32, [i32, i64, i64, i64, i32, ctypes.c_char_p, ctypes.c_size_t]),
@@ -191,11 +193,29 @@ def qblk_gemv_f32_work_bytes(batch, k):
     return int(_load().qblk_gemv_f32_work_bytes(int(batch), int(k)))
 
 
+def qblk_gemv_f32_fallback_offset(batch, k):
+    return int(_load().qblk_gemv_f32_fallback_offset(int(batch), int(k)))
+
+
+def qblk_gemv_f32_set_wait_limit(ticks):
+    """Test setting: the in-launch handoff's wait bound for this thread's
+    later launches (100 MHz ticks; negative restores the 20 ms default)."""
+    _check(_load().qblk_gemv_f32_set_wait_limit(int(ticks)), "qblk_gemv_f32_set_wait_limit")
+
+
+def handoff_fallbacks(work, batch, k):
+    """The fallback counter inside a qblk_gemv_f32 workspace (a device read)."""
+    off = qblk_gemv_f32_fallback_offset(batch, k)
+    return int(work[off:off + 4].view(__import__("torch").int32).item())
+
+
 def qblk_gemv_f32(wtype, wq, n, k, x, batch=None, y=None, work=None, stream=None):
     """y[b, :n] = W quant(x_b): activation quantization fused into the GEMV.
     x: float32 [batch, >= k] device tensor with unit stride along rows.
     work: uint8 device workspace of qblk_gemv_f32_work_bytes(batch, k) bytes
-    (allocated here when None); calls that may overlap need their own."""
+    (allocated and zeroed here when None); calls that may overlap need their
+    own. Its fallback counter (handoff_fallbacks) counts only if the caller
+    zeroed the workspace once."""
     import torch
     _require_cuda(wq, "wq")
     _require_cuda(x, "x", rows=True)
@@ -212,7 +232,7 @@ def qblk_gemv_f32(wtype, wq, n, k, x, batch=None, y=None, work=None, stream=None
         raise ValueError("wq smaller than the packed size")
     need = qblk_gemv_f32_work_bytes(batch, k)
     if work is None:
-        work = torch.empty(max(need, 1), dtype=torch.uint8, device=wq.device)
+        work = torch.zeros(max(need, 1), dtype=torch.uint8, device=wq.device)
     _require_cuda(work, "work")
     if work.numel() < need:
         raise ValueError("work smaller than qblk_gemv_f32_work_bytes(batch, k)")

@@ -219,8 +219,8 @@ qblk_status qblk_gemv_multi(int type, const qblk_gemv_desc *descs, int count, in
  *     into `work`, one 64-block slice of one row each, and publish each slice
  *     with a tag unique to the launch; the workgroups issue their first
  *     weight loads, then wait for the tags (a bounded wait: past about 20 ms
- *     a workgroup quantizes the rows itself, so the result never depends on
- *     scheduling).
+ *     a workgroup adds 1 to the workspace's fallback counter and quantizes
+ *     the rows itself, so the result never depends on scheduling).
  *   x    : fp32 [batch][ldx];  other arguments as qblk_gemv.
  *   work : device workspace of qblk_gemv_f32_work_bytes(batch, k) bytes,
  *          256-byte aligned, owned by the caller. It holds no state that a
@@ -234,6 +234,18 @@ qblk_status qblk_gemv_multi(int type, const qblk_gemv_desc *descs, int count, in
  */
 int qblk_gemv_f32_max_batch(int64_t k);
 size_t qblk_gemv_f32_work_bytes(int64_t batch, int64_t k); /* 0 if invalid */
+/* Byte offset inside the workspace of a uint32 counter that every launch
+ * with the in-launch handoff increments once per workgroup that stopped
+ * waiting and quantized the activation itself (0 if batch or k is invalid).
+ * The library never resets it: a caller that zeroes it once can read how
+ * often the fallback ran. */
+size_t qblk_gemv_f32_fallback_offset(int64_t batch, int64_t k);
+/* Test setting: the handoff's wait bound, in ticks of the 100 MHz realtime
+ * counter, for launches made later from the calling thread (thread-local;
+ * a negative value restores the default of 2,000,000 = 20 ms). A bound of 0
+ * makes every workgroup that finds a slice unpublished take the fallback at
+ * once; results are identical either way. */
+qblk_status qblk_gemv_f32_set_wait_limit(int64_t ticks);
 qblk_status qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const float *x,
                   int64_t ldx, int64_t batch, float *y, int64_t ldy, void *work,
                   hipStream_t stream);

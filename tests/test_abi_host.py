@@ -266,3 +266,15 @@ def test_benchmarked_gemv_instances_have_parity_cases():
         if v not in covered:
             missing[c] = v
     assert not missing, missing
+
+
+def test_gemv_f32_fallback_counter_location():
+    for batch, k in ((1, 4096), (4, 8192), (8, 28672), (3, 2304)):
+        off = qblk.qblk_gemv_f32_fallback_offset(batch, k)
+        assert off % 256 == 0
+        assert off >= qblk.qblk_act_bytes(batch, k)
+        assert off + 4 <= qblk.qblk_gemv_f32_work_bytes(batch, k)
+    assert qblk.qblk_gemv_f32_fallback_offset(9, 4096) == 0
+    assert qblk.qblk_gemv_f32_fallback_offset(1, 100) == 0
+    assert qblk.lib().qblk_gemv_f32_set_wait_limit(0) == OK
+    assert qblk.lib().qblk_gemv_f32_set_wait_limit(-1) == OK

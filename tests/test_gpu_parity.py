@@ -361,6 +361,7 @@ def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
     wq = dev_pack(wtype, w)
     work = t.randint(0, 256, (qblk.qblk_gemv_f32_work_bytes(batch, k),), dtype=t.uint8,
                      device="cuda")
+    fallbacks0 = qblk.handoff_fallbacks(work, batch, k)
     for call in range(3):
         x = rng.standard_normal((batch, k)).astype(np.float32)
         if call == 1:
@@ -369,6 +370,8 @@ def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
         fused = host(qblk.qblk_gemv_f32(wtype, wq, n, k, xd, work=work))
         two_step = host(qblk.qblk_gemv(wtype, wq, n, k, qblk.qblk_quantize_act(xd), batch))
         assert np.array_equal(fused.view(np.uint32), two_step.view(np.uint32)), call
+    # no workgroup gave up waiting for the producers
+    assert qblk.handoff_fallbacks(work, batch, k) == fallbacks0
     if k <= 28672:
         rows = _sample_rows(n, 16, n)
         check_rel(fused[:, rows], expected(wtype, w[rows], x))
@@ -395,6 +398,44 @@ def test_gemv_f32_70b_decode_shapes_sampled(name, n, k, batch):
     del w, wq
     t.cuda.empty_cache()
     check_rel(fused[:, rows], expected(o.TYPE_Q4_K, w_rows, x))
+
+
+@pytest.mark.parametrize("wtype", [o.TYPE_Q4_K, o.TYPE_Q8_0])
+@pytest.mark.parametrize("n,k,batch", [(9000, 8192, 1), (16400, 8192, 4), (16400, 2304, 3),
+                                       (3, 1 << 20, 4)])
+def test_gemv_f32_handoff_fallback_is_bit_exact(wtype, n, k, batch):
+    """With the handoff's wait bound set to 0 ticks every workgroup that
+    finds a slice unpublished quantizes the whole activation itself, racing
+    the producers over the same workspace bytes: the result is still bitwise
+    that of quantize + qblk_gemv, and the workspace counter records the
+    fallbacks. (3, 2^20, 4): one workgroup, which publishes every slice itself
+    before it waits."""
+    if wtype == o.TYPE_Q4_K and k % 256:
+        pytest.skip("Q4_K needs k % 256 == 0")
+    t = torch()
+    print(f"gemv_f32 forced fallback {TNAME[wtype]} n={n} k={k} batch={batch}", flush=True)
+    rng = np.random.default_rng(17 * wtype + n + batch)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    wq = dev_pack(wtype, w)
+    work = t.zeros(qblk.qblk_gemv_f32_work_bytes(batch, k), dtype=t.uint8, device="cuda")
+    x = dev(rng.standard_normal((batch, k)).astype(np.float32))
+    two_step = host(qblk.qblk_gemv(wtype, wq, n, k, qblk.qblk_quantize_act(x), batch))
+    qblk.qblk_gemv_f32_set_wait_limit(0)
+    try:
+        for call in range(2):
+            fused = host(qblk.qblk_gemv_f32(wtype, wq, n, k, x, work=work))
+            assert np.array_equal(fused.view(np.uint32), two_step.view(np.uint32)), call
+    finally:
+        qblk.qblk_gemv_f32_set_wait_limit(-1)
+    fb = qblk.handoff_fallbacks(work, batch, k)
+    print(f"  fallbacks: {fb}", flush=True)
+    if n >= 9000:
+        assert fb > 0
+    # the default bound again: no fallback
+    work.zero_()
+    fused = host(qblk.qblk_gemv_f32(wtype, wq, n, k, x, work=work))
+    assert np.array_equal(fused.view(np.uint32), two_step.view(np.uint32))
+    assert qblk.handoff_fallbacks(work, batch, k) == 0
 
 
 def test_gemv_f32_strided_rows_and_limits():
