@@ -1,6 +1,6 @@
 """Build libqblk.so (gfx950) in-tree with hipcc.
 
-    python -m block_quantized_qblk_amd.build_lib
+    python -m block_quantized_qblk_amd.build_lib [--changed]
 
 Objects go to <repo>/_build/, the shared library next to this file.
 """
@@ -69,12 +69,27 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True):
-    """Compile every source and link libqblk.so. Always recompiles."""
+def _stale(src):
+    """Whether src's object is missing or older than src or any header."""
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(d, f) for d in (CSRC, os.path.join(ROOT, "include"))
+                                        for f in os.listdir(d) if f.endswith(".h")]
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose=True, changed_only=False):
+    """Compile the sources and link libqblk.so. Recompiles every source
+    unless changed_only (then only those whose object is older than the
+    source or a header)."""
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    todo = [s for s in SOURCES if not changed_only or _stale(s)]
+    jobs = min(max(1, len(todo)), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-o", tmp] + objs + [f"--offload-arch={ARCH}", "-fPIC"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -87,4 +102,4 @@ def build(verbose=True):
 
 
 if __name__ == "__main__":
-    build()
+    build(changed_only="--changed" in sys.argv[1:])
