@@ -34,6 +34,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 constexpr int64_t kMaxGridThreads = (int64_t{1} << 32) - 256;
 
 static_assert(QBLK_GEMV_MULTI_MAX == qblk::kGemvMultiMax, "descriptor list sizes agree");
+static_assert(QBLK_NOALLOC_MAX_K == qblk::kNoallocMaxK && QBLK_NOALLOC_MAX_ACT_BYTES == qblk::kNoallocMaxActBytes,
+              "allocation-free limits agree");
 
 qblk_status finish(hipError_t e) {
   if (e != hipSuccess) {
@@ -147,7 +149,27 @@ QBLK_EXPORT qblk_status qblk_gemv_f32(int type, const void* wq, int64_t n, int64
   if (batch > qblk::gemv_f32_max_batch(k)) return QBLK_ERR_UNSUPPORTED;
   if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
-  return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, work, g_wait_ticks, stream));
+  return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy,
+                                      qblk::gemv_work_in(work, batch, k), g_wait_ticks, stream));
+}
+
+QBLK_EXPORT qblk_status qblk_gemv_f32_noalloc(int type, const void* wq, int64_t n, int64_t k,
+                                              const float* x, int64_t ldx, int64_t batch, float* y,
+                                              int64_t ldy, hipStream_t stream) {
+  const qblk_status st = check_product(type, wq, n, k, x, batch, y, ldy);
+  if (st != QBLK_OK || n == 0 || batch == 0) return st;
+  if (ldx < k) return QBLK_ERR_SHAPE;
+  if (!aligned(x, 16) || ldx % 4 != 0) return QBLK_ERR_ALIGN;
+  if (batch > qblk::gemv_f32_max_batch(k) || k > qblk::kNoallocMaxK ||
+      static_cast<int64_t>(qblk_act_bytes(batch, k)) > qblk::kNoallocMaxActBytes)
+    return QBLK_ERR_UNSUPPORTED;
+  if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  qblk::GemvWork w{};
+  const hipError_t e = qblk::gemv_scratch_work(stream, &w);
+  if (e == hipErrorInvalidDevice) return QBLK_ERR_ARG;
+  if (e != hipSuccess) return finish(e);
+  (void)hipGetLastError();
+  return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy, w, g_wait_ticks, stream));
 }
 
 QBLK_EXPORT size_t qblk_gemv_f32_fallback_offset(int64_t batch, int64_t k) {

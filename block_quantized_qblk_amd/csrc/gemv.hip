@@ -16,6 +16,8 @@
 // so loads need no per-lane 64-bit address arithmetic. Per block:
 // v_dot4_i32_i8 on unpacked nibbles (or int8 codes), then one or two fp32 FMAs
 // with the block scales; a DPP wave reduction at the end.
+#include <atomic>
+
 #include "qblk_device.h"
 
 namespace qblk {
@@ -551,9 +553,7 @@ struct Plan {
   int64_t ldy;
   const float* x;     // fp32 activations (fused variants)
   int64_t ldx;
-  uint8_t* work;      // SYNC: workspace (activation buffer, flags, fallback counter)
-  int64_t flags_off;
-  int64_t fallback_off;
+  GemvWork work;      // SYNC: activation buffer, flags, fallback counter
   int64_t wait_ticks;
 };
 
@@ -570,12 +570,12 @@ inline GemvArgs make_args(const Plan& p) {
   g.ads = p.A.ds;
   g.y = p.y;
   g.ldy = p.ldy;
-  g.xq_codes = p.work;
-  g.xq_ds = p.work ? p.work + (p.A.ds - p.A.q) : nullptr;
-  g.flags = p.work ? reinterpret_cast<uint64_t*>(p.work + p.flags_off) : nullptr;
+  g.xq_codes = p.work.act;
+  g.xq_ds = p.work.act ? p.work.act + (p.A.ds - p.A.q) : nullptr;
+  g.flags = p.work.flags;
   g.nslices = static_cast<uint32_t>((p.nb + 63) / 64);
   g.flag_stride = static_cast<uint32_t>(gemv_flag_stride(p.nb * 32));
-  g.fallbacks = p.work ? reinterpret_cast<uint32_t*>(p.work + p.fallback_off) : nullptr;
+  g.fallbacks = p.work.fallbacks;
   g.wait_ticks = static_cast<uint64_t>(p.wait_ticks);
   return g;
 }
@@ -782,7 +782,7 @@ hipError_t launch_gemv_multi(int type, const GemvDesc* d, int count, int64_t bat
 // others wait for it behind their first weight loads (repeating the
 // quantization in every workgroup would cost more than the weight stream).
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
-                           int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
+                           int64_t ldx, int64_t batch, float* y, int64_t ldy, const GemvWork& work,
                            int64_t wait_ticks, hipStream_t s) {
   Plan p{};
   p.W.base = static_cast<const uint8_t*>(wq);
@@ -799,12 +799,48 @@ hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const
     p.A = make_act(nullptr, 0, k);
     return launch_type<kLdsFused>(type, bc, p, s);
   }
-  p.A = make_act(work, batch, k);
-  p.work = static_cast<uint8_t*>(work);
-  p.flags_off = gemv_flags_offset(batch, k);
-  p.fallback_off = gemv_fallback_offset(batch, k);
+  p.A = make_act(work.act, batch, k);
+  p.work = work;
   p.wait_ticks = wait_ticks;
   return launch_type<kInLaunch>(type, bc, p, s);
+}
+
+// ---------------------------------------------------------------- fixed workspace
+// The allocation-free entry point's workspace (qblk_gemv_f32_noalloc): a
+// file-scope device array, zero when the code object is loaded. Each GPU the
+// library runs on holds its own copy until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: kernels get
+// the address from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<uint8_t*> g_scratch_addr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t gemv_scratch_work(hipStream_t stream, GemvWork* w) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  if (stream != nullptr) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    if (static_cast<int>(sd) != dev) return hipErrorInvalidDevice;
+  }
+  uint8_t* base = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (base == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    base = static_cast<uint8_t*>(p);
+    g_scratch_addr[dev].store(base, std::memory_order_release);
+  }
+  w->flags = reinterpret_cast<uint64_t*>(base);
+  w->fallbacks = reinterpret_cast<uint32_t*>(base + kScratchFlagBytes - 256);
+  w->act = base + kScratchFlagBytes;
+  return hipSuccess;
 }
 
 }  // namespace qblk

@@ -110,9 +110,37 @@ struct GemvVariant {
 };
 GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode);
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len);
+// Where the in-launch handoff keeps its data: the activation buffer
+// (qblk_quantize_act layout, batch rows of k), the 8 flag copies of
+// gemv_flag_stride(k) u64 each, and the fallback counter.
+struct GemvWork {
+  uint8_t* act;
+  uint64_t* flags;
+  uint32_t* fallbacks;
+};
+// ... inside a caller's workspace of gemv_f32_work_bytes(batch, k) bytes
+inline GemvWork gemv_work_in(void* work, int64_t batch, int64_t k) {
+  uint8_t* b = static_cast<uint8_t*>(work);
+  return GemvWork{b, reinterpret_cast<uint64_t*>(b + gemv_flags_offset(batch, k)),
+                  reinterpret_cast<uint32_t*>(b + gemv_fallback_offset(batch, k))};
+}
+// ... inside the library's fixed device array (the allocation-free entry
+// point): flags from byte 0, the counter at kScratchFlagBytes - 256, the
+// activation buffer from kScratchFlagBytes. The flag region holds 8 copies
+// of gemv_flag_stride(k) u64 for k <= kNoallocMaxK.
+constexpr int64_t kScratchBytes = int64_t(1) << 20;
+constexpr int64_t kScratchFlagBytes = int64_t(64) << 10;
+constexpr int64_t kNoallocMaxActBytes = kScratchBytes - kScratchFlagBytes;  // 983040
+constexpr int64_t kNoallocMaxK = int64_t(1) << 17;
+static_assert(8 * 8 * ((8 * ((kNoallocMaxK / 32 + 63) / 64) + 15) / 16 * 16) <= kScratchFlagBytes - 256,
+              "flag copies fit the flag region");
+// The fixed array's GemvWork on the current device, after checking that
+// `stream` belongs to it (hipErrorInvalidDevice if not). The array's address
+// is looked up once per device, on the first call made there.
+hipError_t gemv_scratch_work(hipStream_t stream, GemvWork* w);
 // wait_ticks: the handoff's wait bound (kGemvWaitTicks outside tests)
 hipError_t launch_gemv_f32(int type, const void* wq, int64_t n, int64_t k, const float* x,
-                           int64_t ldx, int64_t batch, float* y, int64_t ldy, void* work,
+                           int64_t ldx, int64_t batch, float* y, int64_t ldy, const GemvWork& work,
                            int64_t wait_ticks, hipStream_t s);
 // one product of a multi-product GEMV launch (quantized activations)
 struct GemvDesc {

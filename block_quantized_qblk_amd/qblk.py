@@ -49,6 +49,7 @@ def _load():
         "qblk_gemv_f32_work_bytes": (ctypes.c_size_t, [i64, i64]),
         "qblk_gemv_f32": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp, vp]),
         "qblk_gemv_f32_fallback_offset": (ctypes.c_size_t, [i64, i64]),
+        "qblk_gemv_f32_noalloc": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]),
         "qblk_gemv_f32_set_wait_limit": (i32, [i64]),
         "qblk_gemv_float": (i32, [i32, vp, i64, i64, vp, i64, i64, vp, i64, vp]),
         "qblk_gemv_multi": (i32, [i32, vp, i32, i64, vp]),
@@ -239,6 +240,25 @@ def qblk_gemv_f32(wtype, wq, n, k, x, batch=None, y=None, work=None, stream=None
     _check(_load().qblk_gemv_f32(_type(wtype), _ptr(wq), int(n), int(k), _ptr(x), x.stride(0),
                                  int(batch), _ptr(y), y.stride(0), _ptr(work), _stream(stream)),
            "qblk_gemv_f32")
+    return y
+
+
+def qblk_gemv_f32_noalloc(wtype, wq, n, k, x, y, batch=None, stream=None):
+    """qblk_gemv_f32 without a workspace (the library's fixed device array;
+    allocates nothing, so y must be given). Calls that overlap on one GPU
+    race on the array."""
+    _require_cuda(wq, "wq")
+    _require_cuda(x, "x", rows=True)
+    _require_cuda(y, "y", rows=True)
+    if batch is None:
+        batch = x.shape[0]
+    if x.shape[1] < k or y.shape[0] < batch or y.shape[1] < n:
+        raise ValueError("x must be [batch, >= k] and y [batch, >= n]")
+    if wq.numel() < qblk_weight_bytes(wtype, n, k):
+        raise ValueError("wq smaller than the packed size")
+    _check(_load().qblk_gemv_f32_noalloc(_type(wtype), _ptr(wq), int(n), int(k), _ptr(x), x.stride(0),
+                                         int(batch), _ptr(y), y.stride(0), _stream(stream)),
+           "qblk_gemv_f32_noalloc")
     return y
 
 

@@ -251,6 +251,31 @@ qblk_status qblk_gemv_f32(int type, const void *wq, int64_t n, int64_t k, const 
                   hipStream_t stream);
 
 /*
+ * qblk_gemv_f32 for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * result, bit for bit, with no workspace argument. The in-launch handoff
+ * uses a fixed device array of the library instead (1 MiB, held by each GPU
+ * the library runs on until the process ends; its address is looked up once
+ * per device, on the first call made there, with hipGetSymbolAddress). The
+ * call allocates and frees nothing.
+ * Limits: batch <= 8, k <= QBLK_NOALLOC_MAX_K and qblk_act_bytes(batch, k)
+ * <= QBLK_NOALLOC_MAX_ACT_BYTES (e.g. k <= 98304 at batch 8); beyond them
+ * QBLK_ERR_UNSUPPORTED, nothing enqueued.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents. Nothing in it has to be cleared between calls (the flags only
+ * ever hold zero or earlier launches' tags, which never match a later one),
+ * but calls that overlap on one GPU race on it: calls from several streams
+ * or threads must be serialized by the caller.
+ * `stream` must belong to the current device (else QBLK_ERR_ARG).
+ * Errors: as qblk_gemv_f32, without the workspace ones.
+ */
+#define QBLK_NOALLOC_MAX_K 131072
+#define QBLK_NOALLOC_MAX_ACT_BYTES 983040
+qblk_status qblk_gemv_f32_noalloc(int type, const void *wq, int64_t n, int64_t k, const float *x,
+                                  int64_t ldx, int64_t batch, float *y, int64_t ldy,
+                                  hipStream_t stream);
+
+/*
  * Introspection (host only, no GPU work): the name of the kernel instance
  * that qblk_gemv (fused == 0) or qblk_gemv_f32 (fused != 0) launches for
  * this shape, for the first group of up to 8 activation rows, as the

@@ -31,9 +31,10 @@ hipError_t launch_gemv(int, const void*, int64_t, int64_t, const void*, int64_t,
   launched("gemv");
 }
 hipError_t launch_gemv_f32(int, const void*, int64_t, int64_t, const float*, int64_t, int64_t, float*, int64_t,
-                           void*, int64_t, hipStream_t) {
+                           const GemvWork&, int64_t, hipStream_t) {
   launched("gemv_f32");
 }
+hipError_t gemv_scratch_work(hipStream_t, GemvWork*) { launched("gemv_scratch_work"); }
 hipError_t launch_gemv_multi(int, const GemvDesc*, int, int64_t, hipStream_t) { launched("gemv_multi"); }
 hipError_t launch_gemv_float(int, const void*, int64_t, int64_t, const float*, int64_t, int64_t, float*, int64_t,
                              hipStream_t) {
