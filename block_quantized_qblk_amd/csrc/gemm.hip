@@ -59,8 +59,7 @@ constexpr int TM = BM / 32 / (kWaves / kWavesN);  // 32-row MFMA tiles per wave
 constexpr int TN = BN / 32 / kWavesN;             // 32-column MFMA tiles per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int kAInstr = BM * 8 / 64 / kWaves;     // activation DMA instructions per wave and stage
-constexpr int kMagicBits = 0x4B400000;  // fp32 1.5 * 2^23
-constexpr float kMagic = 12582912.0f;
+// kMagicBits / kMagic (fp32 1.5 * 2^23): qblk_device.h
 
 // Min-term operands of a step in LDS (Q4_K: d_act * code sum and d_min * mn;
 // Q4_0: d_act * code sum and -8 d); Q8_0 has no min term.

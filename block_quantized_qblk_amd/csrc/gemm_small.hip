@@ -43,8 +43,7 @@ constexpr int kSb = 8;  // blocks per scale chunk (one Q4_K super-block)
 // waves per workgroup = ways the k range is split (measured on MI355X: 8 or
 // 16 waves, or loads a whole chunk ahead, are slower for 1..64 rows)
 constexpr int kWaves = 4;
-constexpr int kMagicBits = 0x4B400000;  // fp32 1.5 * 2^23
-constexpr float kMagic = 12582912.0f;
+// kMagicBits / kMagic (fp32 1.5 * 2^23): qblk_device.h
 
 template <int TYPE>
 constexpr bool kHasMin = TYPE != kQ8_0;

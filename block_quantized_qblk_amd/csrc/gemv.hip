@@ -192,14 +192,19 @@ __device__ __forceinline__ void block_fma(uint32_t lane, const WChunk<TYPE>& w,
                                           const WScale<TYPE>& s, const uint4 (&a)[B][U][2],
                                           const float2 (&ds)[B][U], int u, float (&acc)[B]) {
   if constexpr (TYPE == kQ4_K) {
+    // sw = d*sc_j has at most 17 significant bits, so -1.5*2^23*sw is an
+    // fp32 number and fma(1.5*2^23 + S, sw, -1.5*2^23*sw) = round(S*sw), one
+    // instruction; then the activation scale and the min term, whose
+    // d_act*A is shared by the wave's rows
     const int j = static_cast<int>(lane & 7);  // sub-block inside the super-block
     const float sw = half_bits_to_float(s.h.x) * static_cast<float>(q4k_sc(s.h, j));
     const float wm = half_bits_to_float(s.h.x >> 16) * static_cast<float>(q4k_mn(s.h, j));
+    const float ncs = -kMagic * sw;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int S = dot_nib32(w.q, a[b][u][0], a[b][u][1]);
-      const float asum = static_cast<float>(__float_as_int(ds[b][u].y));
-      acc[b] = fmaf(ds[b][u].x, fmaf(sw, static_cast<float>(S), wm * asum), acc[b]);
+      const float t = fmaf(dot_nib32_magic(w.q, a[b][u][0], a[b][u][1]), sw, ncs);
+      const float dA = ds[b][u].x * static_cast<float>(__float_as_int(ds[b][u].y));
+      acc[b] = fmaf(wm, dA, fmaf(t, ds[b][u].x, acc[b]));
     }
   } else if constexpr (TYPE == kQ4_0 || TYPE == kQ4_0H) {
 #pragma unroll

@@ -69,6 +69,34 @@ __device__ __forceinline__ int dot_nib32(uint4 w, uint4 a0, uint4 a1) {
   return acc;
 }
 
+// The fp32 number 1.5 * 2^23 and its bit pattern. An int32 dot chain that
+// starts from the bit pattern (instead of 0) ends at the bit pattern of the
+// float 1.5 * 2^23 + S, exactly, for |S| < 2^22 (every block dot here).
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
+
+// First product of a chain that starts at kMagicBits (held in a scalar
+// register, the three-operand dot).
+__device__ __forceinline__ int dot4_magic(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot4_i32_i8 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(kMagicBits));
+  return r;
+}
+
+// dot_nib32 read as fp32: 1.5 * 2^23 + S, exactly.
+__device__ __forceinline__ float dot_nib32_magic(uint4 w, uint4 a0, uint4 a1) {
+  const uint32_t m = 0x0F0F0F0Fu;
+  int acc = dot4_magic(w.x & m, a0.x);
+  acc = dot4((w.x >> 4) & m, a0.y, acc);
+  acc = dot4(w.y & m, a0.z, acc);
+  acc = dot4((w.y >> 4) & m, a0.w, acc);
+  acc = dot4(w.z & m, a1.x, acc);
+  acc = dot4((w.z >> 4) & m, a1.y, acc);
+  acc = dot4(w.w & m, a1.z, acc);
+  acc = dot4((w.w >> 4) & m, a1.w, acc);
+  return __int_as_float(acc);
+}
+
 // 32 int8 codes against 32 int8 codes, both in the same per-group order.
 __device__ __forceinline__ int dot_i8x32(uint4 w0, uint4 w1, uint4 a0, uint4 a1) {
   int acc = dot4_zero(w0.x, a0.x);
