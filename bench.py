@@ -457,10 +457,13 @@ DOMINANT_KERNEL = "gemv_kernel<3, 1, 4, 1, true, true>"  # <Q4_K, batch, rows/wa
 DOMINANT_GROUPS = ("gate_up",)
 GEMV_TRAFFIC = os.path.join(ROOT, "profiles", "gemv_q4k_70b_decode_traffic.md")
 GEMV_SOURCES = ["block_quantized_qblk_amd/csrc/gemv.hip",
-                "block_quantized_qblk_amd/csrc/qblk_device.h"]
+                "block_quantized_qblk_amd/csrc/gemv_select.cpp",
+                "block_quantized_qblk_amd/csrc/qblk_device.h",
+                "block_quantized_qblk_amd/csrc/qblk_internal.h"]
 GEMM_TRAFFIC = os.path.join(ROOT, "profiles", "gemm_q4k_512x14336x4096.md")
 GEMM_SOURCES = ["block_quantized_qblk_amd/csrc/gemm.hip",
-                "block_quantized_qblk_amd/csrc/qblk_device.h"]
+                "block_quantized_qblk_amd/csrc/qblk_device.h",
+                "block_quantized_qblk_amd/csrc/qblk_internal.h"]
 
 
 def sources_sha256(sources):
