@@ -119,7 +119,7 @@ __device__ __forceinline__ void quantize_slice(const GemvArgs& g, uint32_t sl) {
   const uint32_t b = sl / g.nslices;
   const uint32_t blk = ((sl - b * g.nslices) << 6) + (threadIdx.x >> 2);
   const uint32_t sub = threadIdx.x & 3;
-  if (blk >= g.nb) return;  // whole quads
+  if (threadIdx.x >= 256u || blk >= g.nb) return;  // whole quads; 64 blocks per slice
   const uint32_t k = g.nb * 32u;
   const float* src = g.x + b * g.ldx + 32u * blk + 8u * sub;
   const float4 v0 = *reinterpret_cast<const float4*>(src);
@@ -164,13 +164,13 @@ __device__ __forceinline__ void produce(const GemvArgs& g, uint64_t tag) {
 // quantizes every slice itself (the same bytes the producers write), so the
 // kernel finishes with the right result even if the producers were never
 // scheduled. All exits are decided by workgroup-wide reductions.
-template <int B>
+template <int B, int WAVES = 4>
 __device__ __forceinline__ void wait_slices(const GemvArgs& g, uint64_t tag) {
   const uint64_t* f = g.flags + (blockIdx.x & 7u) * g.flag_stride;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   while (true) {
     int pending = 0;
-    for (uint32_t sl = threadIdx.x; sl < B * g.nslices; sl += 256u)
+    for (uint32_t sl = threadIdx.x; sl < B * g.nslices; sl += 64u * WAVES)
       pending |= __hip_atomic_load(f + sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag;
     if (!__syncthreads_or(pending)) return;
     const int late = __builtin_amdgcn_s_memrealtime() - t0 > g.wait_ticks;  // 100 MHz clock
@@ -231,19 +231,19 @@ __device__ __forceinline__ void block_fma(uint32_t lane, const WChunk<TYPE>& w,
 // of codes the (d, sum) pairs, [B][nb].
 // (act_lds_row, act_lds_bytes and the staging limits: qblk_internal.h)
 
-template <int B>
+template <int B, int WAVES = 4>
 __device__ __forceinline__ void stage_acts(const GemvArgs& g, uint8_t* smem) {
   const uint32_t k = g.nb * 32u, kp = act_lds_row(g.nb);
 #pragma unroll
   for (int b = 0; b < B; ++b) {
-    for (uint32_t u = threadIdx.x; u < k / 16u; u += 256u) {
+    for (uint32_t u = threadIdx.x; u < k / 16u; u += 64u * WAVES) {
       const uint32_t blk = u >> 1, h = u & 1u;
       *reinterpret_cast<uint4*>(smem + b * kp + (((blk >> 6) * 2u + h) << 10) + ((blk & 63u) << 4)) =
           load16(g.aq + b * k + 16u * u);
     }
   }
   uint8_t* sds = smem + B * kp;
-  for (uint32_t i = threadIdx.x; i < B * g.nb; i += 256u)
+  for (uint32_t i = threadIdx.x; i < B * g.nb; i += 64u * WAVES)
     *reinterpret_cast<uint2*>(sds + 8u * i) = *reinterpret_cast<const uint2*>(g.ads + 8u * i);
 }
 
@@ -276,12 +276,12 @@ __device__ __forceinline__ void load_act_block(const GemvArgs& g, const uint8_t*
 // chunks' weight loads are issued before the wait / staging.
 // `block` is the workgroup's index within this product (blockIdx.x, or its
 // offset inside a descriptor's range for the multi-product launch).
-template <int TYPE, int B, int R, int U, bool SYNC, bool ALDS>
+template <int TYPE, int B, int R, int U, bool SYNC, bool ALDS, int WAVES = kWavesPerBlock>
 __device__ __forceinline__ void gemv_body(const GemvArgs& g, uint32_t block) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr bool kAllWaves = SYNC || ALDS;  // workgroup barriers ahead: no early exit
   const uint32_t lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(block) * kWavesPerBlock +
+  const int64_t wave = static_cast<int64_t>(block) * WAVES +
                        __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t row0 = wave * R;
   uint64_t tag = 0;
@@ -347,9 +347,9 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& g, uint32_t block) {
     WChunk<TYPE> w2[R][U];
     WScale<TYPE> s2[R][U];
     if constexpr (kPre2) load_weights(U, w2, s2);
-    if constexpr (SYNC) wait_slices<B>(g, tag);
+    if constexpr (SYNC) wait_slices<B, WAVES>(g, tag);
     if constexpr (ALDS) {
-      stage_acts<B>(g, smem);
+      stage_acts<B, WAVES>(g, smem);
       __syncthreads();
     }
     if (!active) return;
@@ -393,9 +393,9 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& g, uint32_t block) {
   }
 }
 
-template <int TYPE, int B, int R, int U, bool SYNC = false, bool ALDS = false>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
-  gemv_body<TYPE, B, R, U, SYNC, ALDS>(g, blockIdx.x);
+template <int TYPE, int B, int R, int U, bool SYNC = false, bool ALDS = false, int WAVES = kWavesPerBlock>
+__global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
+  gemv_body<TYPE, B, R, U, SYNC, ALDS, WAVES>(g, blockIdx.x);
 }
 
 // Several independent products in one launch (a descriptor list, e.g. the
@@ -608,15 +608,15 @@ hipError_t launch_pipe(const Plan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int TYPE, int B, int R, int U, bool SYNC>
+template <int TYPE, int B, int R, int U, bool SYNC, int WAVES = kWavesPerBlock>
 hipError_t launch_cfg(const Plan& p, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(((p.n + R - 1) / R + WAVES - 1) / WAVES));
   if (stage_in_lds(B, p.nb)) {
-    hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U, SYNC, true>), grid_for<R>(p.n),
-                       dim3(64 * kWavesPerBlock), act_lds_bytes(B, static_cast<uint32_t>(p.nb)),
-                       s, make_args(p));
+    hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U, SYNC, true, WAVES>), grid, dim3(64 * WAVES),
+                       act_lds_bytes(B, static_cast<uint32_t>(p.nb)), s, make_args(p));
   } else {
-    hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U, SYNC, false>), grid_for<R>(p.n),
-                       dim3(64 * kWavesPerBlock), 0, s, make_args(p));
+    hipLaunchKernelGGL((gemv_kernel<TYPE, B, R, U, SYNC, false, WAVES>), grid, dim3(64 * WAVES), 0, s,
+                       make_args(p));
   }
   return hipGetLastError();
 }
@@ -641,6 +641,11 @@ hipError_t launch_b(const Plan& p, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   } else {
+    if (v.waves == 8) {
+      if (ru == 81) return launch_cfg<TYPE, B, 8, 1, SYNC, 8>(p, s);
+      if (ru == 41) return launch_cfg<TYPE, B, 4, 1, SYNC, 8>(p, s);
+      return hipErrorInvalidValue;
+    }
     switch (ru) {
       case 81: return launch_cfg<TYPE, B, 8, 1, SYNC>(p, s);
       case 41: return launch_cfg<TYPE, B, 4, 1, SYNC>(p, s);

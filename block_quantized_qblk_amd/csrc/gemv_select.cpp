@@ -21,6 +21,7 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
   GemvVariant v{};
   v.type = type;
   v.b = b;
+  v.waves = 4;
   v.sync = mode == kGemvInLaunch;
   v.fused = mode == kGemvLdsFused;
   const int64_t nb = k / 32;
@@ -65,6 +66,13 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
     // 9.6 against 9.7 us at batch 4, 13.6 against 14.7 at 8)
     if (b >= 4 && k >= 16384) return set(8, 1);
     if (k <= 4096) return set(2, 1);
+    // Q4_K, 6k-8k rows of 8k weights: 8-wave workgroups, one per compute
+    // unit, so each CU stages the activation rows once instead of twice
+    // (70B-shaped o, 8192 x 8192, in-launch handoff: 11.7 against 13.0 us
+    // at batch 2, 13.2 against 15.6 at 4, 20.3 against 21.4 at 8; with
+    // 10240 rows, 320 such workgroups on 256 CUs, slower: 18.5 against 18.2
+    // at batch 4)
+    if (type == kQ4_K && n > 6144 && n <= 8192 && k <= 8192) v.waves = 8;
     return set(4, 1);
   }
   return set(1, 1);
@@ -76,6 +84,8 @@ int gemv_variant_name(const GemvVariant& v, char* buf, size_t len) {
   if (v.pipe)
     return snprintf(buf, len, "gemv_pipe_kernel<%d, %d, %d, %s, %s, %s>", v.type, v.b, v.r,
                     v.fused ? "true" : "false", t, a);
+  if (v.waves != 4)
+    return snprintf(buf, len, "gemv_kernel<%d, %d, %d, %d, %s, %s, %d>", v.type, v.b, v.r, v.u, t, a, v.waves);
   return snprintf(buf, len, "gemv_kernel<%d, %d, %d, %d, %s, %s>", v.type, v.b, v.r, v.u, t, a);
 }
 

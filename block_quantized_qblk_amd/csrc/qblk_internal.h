@@ -107,6 +107,7 @@ struct GemvVariant {
   bool sync;  // activation quantized once per launch (in-launch handoff)
   bool alds;  // activation rows staged in LDS
   bool fused; // activation quantized in every workgroup's LDS
+  int waves;  // waves per workgroup (classic kernel)
 };
 GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode);
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len);

@@ -44,7 +44,10 @@ GEMV_F32_IN_LAUNCH = [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1), (4096
                       # 8 rows per wave with the activations in LDS (gate/up at
                       # batch 4), 4 rows per wave (q/k/v and o at batch 4), and
                       # their batch-1 controls
-                      (16400, 8192, 4), (9000, 8192, 4), (16400, 8192, 1)]
+                      (16400, 8192, 4), (9000, 8192, 4), (16400, 8192, 1),
+                      # Q4_K's 8-wave workgroups (6k-8k rows of 8k weights, batch
+                      # 2-8), with a ragged last workgroup at 6200 rows
+                      (6200, 8192, 2), (8192, 8192, 8)]
 
 # qblk_gemv_f32 at the 70B-shaped decode's own matrices (q/k/v and gate/up
 # concatenated by rows), Q4_K, sampled rows: (name, n, k) x batch
