@@ -453,7 +453,7 @@ def main():
 # ---------------------------------------------------------------- HBM traffic
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DOMINANT_KERNEL = "gemv_kernel<3, 1, 4, 1, true, true>"  # <Q4_K, batch, rows/wave, chunks, in-launch quantization, activations in LDS>
+DOMINANT_KERNEL = "gemv_kernel<3, 1, 4, 1, true, true, 4>"  # <Q4_K, batch, rows/wave, chunks, in-launch quantization, activations in LDS, waves/workgroup>
 DOMINANT_GROUPS = ("gate_up",)
 GEMV_TRAFFIC = os.path.join(ROOT, "profiles", "gemv_q4k_70b_decode_traffic.md")
 GEMV_SOURCES = ["block_quantized_qblk_amd/csrc/gemv.hip",

@@ -84,9 +84,9 @@ int gemv_variant_name(const GemvVariant& v, char* buf, size_t len) {
   if (v.pipe)
     return snprintf(buf, len, "gemv_pipe_kernel<%d, %d, %d, %s, %s, %s>", v.type, v.b, v.r,
                     v.fused ? "true" : "false", t, a);
-  if (v.waves != 4)
-    return snprintf(buf, len, "gemv_kernel<%d, %d, %d, %d, %s, %s, %d>", v.type, v.b, v.r, v.u, t, a, v.waves);
-  return snprintf(buf, len, "gemv_kernel<%d, %d, %d, %d, %s, %s>", v.type, v.b, v.r, v.u, t, a);
+  // every template argument, the waves per workgroup included, as the
+  // kernel's name reads in a profiler's trace
+  return snprintf(buf, len, "gemv_kernel<%d, %d, %d, %d, %s, %s, %d>", v.type, v.b, v.r, v.u, t, a, v.waves);
 }
 
 }  // namespace qblk

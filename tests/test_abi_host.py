@@ -233,12 +233,14 @@ def test_gemv_multi_validation():
 
 def test_gemv_variant_names():
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 1, True) == \
-        "gemv_kernel<3, 1, 4, 1, true, true>"
+        "gemv_kernel<3, 1, 4, 1, true, true, 4>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 4, True) == \
-        "gemv_kernel<3, 4, 8, 1, true, true>"
+        "gemv_kernel<3, 4, 8, 1, true, true, 4>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 1024, 2048, 1, True).startswith("gemv_pipe_kernel<3, 1, 2, true")
     assert qblk.qblk_gemv_variant(o.TYPE_Q8_0, 14336, 4096, 1, False) == \
-        "gemv_kernel<2, 1, 2, 2, false, true>"
+        "gemv_kernel<2, 1, 2, 2, false, true, 4>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 8192, 4, True) == \
+        "gemv_kernel<3, 4, 4, 1, true, true, 8>"
     lib = qblk.lib()
     buf = ctypes.create_string_buffer(8)
     assert lib.qblk_gemv_variant(3, 57344, 8192, 1, 1, buf, 8) == ERR_ARG      # too short
