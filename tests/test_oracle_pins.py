@@ -113,16 +113,13 @@ def test_q4_0_f16_scale_is_nearest_half_of_amax_over_7():
 
 # ---------------------------------------------------------------- scalar kernel of §6.4
 
-def _page_q4_0_float_dot(packed_row, K, yf):
-    """The scalar Q4_0 dot of runguoli page §6.4, restated: for every block,
-    take its scale; for every byte j of the block, low nibble - 8 pairs with
-    float activation 2j and high nibble - 8 with 2j+1; accumulate
-    (code * scale) * activation. Reads the library's row layout."""
-    nb = K // 32
-    scales = packed_row[:4 * nb].copy().view("<f4")
-    qs = packed_row[o.header_bytes(o.TYPE_Q4_0, K):]
+def _page_q4_0_scalar_dot(scales, qs, yf):
+    """The scalar Q4_0 dot of runguoli page §6.4, restated once for both scale
+    widths: for every block, take its scale; for every byte j of the block,
+    low nibble - 8 pairs with float activation 2j and high nibble - 8 with
+    2j+1; accumulate (code * scale) * activation."""
     total = 0.0
-    for blk in range(nb):
+    for blk in range(len(scales)):
         scale = float(scales[blk])
         for j in range(16):
             byte = int(qs[16 * blk + j])
@@ -131,6 +128,13 @@ def _page_q4_0_float_dot(packed_row, K, yf):
             total += (lo * scale) * float(yf[32 * blk + 2 * j])
             total += (hi * scale) * float(yf[32 * blk + 2 * j + 1])
     return total
+
+
+def _page_q4_0_float_dot(packed_row, K, yf):
+    """The page's scalar kernel on the library's Q4_0 row (fp32 scales)."""
+    nb = K // 32
+    scales = packed_row[:4 * nb].copy().view("<f4")
+    return _page_q4_0_scalar_dot(scales, packed_row[o.header_bytes(o.TYPE_Q4_0, K):], yf)
 
 
 def test_q4_0_pack_matches_page_scalar_kernel():
@@ -150,22 +154,12 @@ def test_q4_0_f16_pack_matches_page_scalar_kernel():
     """The same scalar kernel reading fp16 scales: the page's 18-byte block."""
     rng = np.random.default_rng(12)
     K = 256
-    nb = K // 32
     w = (rng.standard_normal((3, K)) * 0.02).astype(np.float32)
     yf = rng.standard_normal(K)
     packed, enc = o.encode_weights(o.TYPE_Q4_0_F16, w)
     deq = o.dequant_weights(o.TYPE_Q4_0_F16, enc)
     for n in range(3):
-        row = packed[n]
-        scales = row[:2 * nb].copy().view("<f2")
-        qs = row[o.header_bytes(o.TYPE_Q4_0_F16, K):]
-        total = 0.0
-        for blk in range(nb):
-            scale = float(scales[blk])
-            for j in range(16):
-                byte = int(qs[16 * blk + j])
-                total += (((byte & 0x0F) - 8) * scale) * float(yf[32 * blk + 2 * j])
-                total += (((byte >> 4) - 8) * scale) * float(yf[32 * blk + 2 * j + 1])
+        total = _page_q4_0_f16_float_dot(packed[n], K, yf)
         ref = float(deq[n] @ yf)
         assert abs(total - ref) <= 1e-12 * max(1.0, abs(ref))
 
@@ -229,18 +223,10 @@ def test_f16_ceil_div_brute_force():
 # ---------------------------------------------------------------- float-activation product
 
 def _page_q4_0_f16_float_dot(packed_row, K, yf):
-    """The runguoli page §6.4 scalar kernel reading the page's fp16 scales."""
+    """The page's scalar kernel reading the page's fp16 scales."""
     nb = K // 32
     scales = packed_row[:2 * nb].copy().view("<f2")
-    qs = packed_row[o.header_bytes(o.TYPE_Q4_0_F16, K):]
-    total = 0.0
-    for blk in range(nb):
-        scale = float(scales[blk])
-        for j in range(16):
-            byte = int(qs[16 * blk + j])
-            total += (((byte & 0x0F) - 8) * scale) * float(yf[32 * blk + 2 * j])
-            total += (((byte >> 4) - 8) * scale) * float(yf[32 * blk + 2 * j + 1])
-    return total
+    return _page_q4_0_scalar_dot(scales, packed_row[o.header_bytes(o.TYPE_Q4_0_F16, K):], yf)
 
 
 def _page_q8_0_float_dot(packed_row, K, yf):
