@@ -371,7 +371,7 @@ __device__ __forceinline__ bool step(const GemmCtx<TYPE>& g, const DmaLanes<TYPE
                                      const ScaleLanes& sl,
                                      const Stage<TYPE>* __restrict__ cur,
                                      Stage<TYPE>* __restrict__ nxt, int64_t st, int64_t steps,
-                                     int tid, int wave, int lane, int wm0, int wn0, int half,
+                                     int tid, int wave, int wm0, int wn0, int half,
                                      int l32, const v16i& cinit, Acc& acc) {
   __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into `cur` are done
   __syncthreads();                // everyone's; the previous readers of `nxt` are done
@@ -435,9 +435,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n,
   issue_codes<TYPE>(g, dl, &s0, 0, wave);
 
   for (int64_t st = 0; st < steps; st += 2) {
-    if (!step<TYPE>(g, dl, sl, &s0, &s1, st, steps, tid, wave, lane, wm0, wn0, half, l32, cinit, acc))
+    if (!step<TYPE>(g, dl, sl, &s0, &s1, st, steps, tid, wave, wm0, wn0, half, l32, cinit, acc))
       break;
-    if (!step<TYPE>(g, dl, sl, &s1, &s0, st + 1, steps, tid, wave, lane, wm0, wn0, half, l32, cinit,
+    if (!step<TYPE>(g, dl, sl, &s1, &s0, st + 1, steps, tid, wave, wm0, wn0, half, l32, cinit,
                     acc))
       break;
   }

@@ -299,7 +299,6 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& g, uint32_t block) {
     const int64_t rr = row0 + r < g.n ? row0 + r : g.n - 1;
     wrow[r] = g.w + rr * g.row_bytes;
   }
-  const uint32_t k = g.nb * 32u;
   const uint32_t nchunks = (g.nb + 63u) >> 6;
 
   float acc[R][B];
@@ -441,7 +440,6 @@ __global__ __launch_bounds__(256) void gemv_pipe_kernel(GemvArgs g) {
   }
   if (!FUSED && !SYNC && !ALDS && row0 >= g.n) return;  // whole wave
   const bool active = row0 < g.n;
-  const uint32_t k = g.nb * 32u;
   const uint32_t nchunks = (g.nb + 63u) >> 6;
   const uint8_t* wrow[R];
 #pragma unroll
