@@ -387,6 +387,7 @@ def main():
     secondary = {}
     if not args.no_secondary:
         secondary["layer_7b"] = layer_7b(torch, qblk, synth, dev, args)
+        secondary["tp8_share"] = tp8_share(torch, qblk, synth, dev, args)
         secondary["gemm"] = gemm_bench(torch, qblk, synth, dev, args.gemm_iters)
         secondary["q4_0_q8_0"] = sym_bench(torch, qblk, synth, dev)
         secondary["kv_scores"] = kv_bench(torch, qblk, synth, dev)
@@ -538,7 +539,7 @@ def gemv_launches(synth):
     kernel instance each one runs must be run by a parity case too."""
     Q4_0, Q8_0, Q4_K = 1, 2, 3
     out = set()
-    for shapes, batches in ((synth.LAYER_70B, (1, 4)), (synth.LAYER_7B, (1,))):
+    for shapes, batches in ((synth.LAYER_70B, (1, 4)), (synth.LAYER_7B, (1,)), (synth.LAYER_70B_TP8, (1,))):
         dims = {name: (n, k) for name, n, k in shapes}
         groups = [(dims["q"][0] + dims["k"][0] + dims["v"][0], dims["q"][1]), dims["o"],
                   (dims["gate"][0] + dims["up"][0], dims["gate"][1]), dims["down"]]
@@ -574,6 +575,27 @@ def layer_7b(torch, qblk, synth, dev, args):
            "rotating_copies": args.copies}
     log(f"7B layer: {res}")
     del graphs, models
+    torch.cuda.empty_cache()
+    return res
+
+
+def tp8_share(torch, qblk, synth, dev, args):
+    """One GPU's share of the 70B-shaped decode token split over 8 GPUs
+    (q/k/v and gate/up by output rows, o and down along K): 80 layers of the
+    shard's own shapes at batch 1, the token as one HIP graph. The
+    collectives the split needs (two all-reduces of 8192 values per layer)
+    are not part of it."""
+    m = DecodeModel(torch, qblk, synth, synth.LAYER_70B_TP8, args.layers, 7000, "student_t", 1, dev)
+    g = m.capture()
+    ms = time_replays(torch, [g], max(10, args.steps // 2), 3)
+    del g
+    tot_b, tot_s, per = m.kernel_times(m.layers)
+    res = {"workload": "q4_k_gemv_70b_decode_tp8_share", "layers": args.layers,
+           "ms_per_token": round(ms, 4), "GBps": round(m.weight_bytes / (ms * 1e-3) / 1e9, 1),
+           "weight_bytes_per_token": m.weight_bytes, "kernel_GBps": round(tot_b / tot_s / 1e9, 1),
+           "per_launch": per, "handoff_fallbacks": m.fallbacks()}
+    log(f"TP=8 share: {res}")
+    del m
     torch.cuda.empty_cache()
     return res
 

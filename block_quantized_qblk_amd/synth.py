@@ -112,6 +112,12 @@ LAYER_70B = [  # one 70B-shaped decoder layer
     ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672),
 ]
 
+LAYER_70B_TP8 = [  # one GPU's share of a 70B-shaped layer split over 8 GPUs (Megatron style):
+    # q, k, v, gate and up split by output rows; o and down split along K (whole super-blocks)
+    ("q", 1024, 8192), ("k", 128, 8192), ("v", 128, 8192), ("o", 8192, 1024),
+    ("gate", 3584, 8192), ("up", 3584, 8192), ("down", 8192, 3584),
+]
+
 WORKLOADS = {
     1: dict(name="q4_0_gemv_4096x4096", type="Q4_0", dist="normal",
             shapes=[("w", 4096, 4096)], m=[1]),

@@ -52,7 +52,10 @@ GEMV_F32_IN_LAUNCH = [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1), (4096
 # qblk_gemv_f32 at the 70B-shaped decode's own matrices (q/k/v and gate/up
 # concatenated by rows), Q4_K, sampled rows: (name, n, k) x batch
 GEMV_F32_70B = [("qkv", 10240, 8192), ("o", 8192, 8192), ("gate_up", 57344, 8192),
-                ("down", 8192, 28672)]
+                ("down", 8192, 28672),
+                # one GPU's share of the same layer split over 8 GPUs
+                ("qkv_tp8", 1280, 8192), ("o_tp8", 8192, 1024), ("gate_up_tp8", 7168, 8192),
+                ("down_tp8", 8192, 3584)]
 GEMV_F32_70B_BATCH = [1, 4]
 
 
