@@ -55,3 +55,36 @@ def test_noalloc_limits():
         with pytest.raises(qblk.QblkError) as ei:
             qblk.qblk_gemv_f32_noalloc(o.TYPE_Q4_K, wq, 8, k, x, y)
         assert ei.value.status == -4
+
+
+def test_noalloc_in_a_graph():
+    """The callers this entry point is for include code under HIP graph
+    capture: captured once, every replay reads the activation in x at replay
+    time (new values are written between replays, with eager use of the same
+    device array in between) and must equal qblk_gemv_f32 run eagerly on them."""
+    print("gemv_f32_noalloc under graph capture", flush=True)
+    t = torch()
+    n, k, batch = 9000, 8192, 2
+    rng = np.random.default_rng(41)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    wq = dev_pack(o.TYPE_Q4_K, w)
+    x = t.empty((batch, k), dtype=t.float32, device="cuda")
+    y = t.empty((batch, n), dtype=t.float32, device="cuda")
+    x.copy_(dev(rng.standard_normal((batch, k)).astype(np.float32)))
+    qblk.qblk_gemv_f32_noalloc(o.TYPE_Q4_K, wq, n, k, x, y)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        qblk.qblk_gemv_f32_noalloc(o.TYPE_Q4_K, wq, n, k, x, y)
+    y_eager = t.empty_like(y)
+    for rep in range(4):
+        x.copy_(dev(rng.standard_normal((batch, k)).astype(np.float32)))
+        # eager use of the same array with other shapes in between
+        small = dev(rng.standard_normal((1, 4096)).astype(np.float32))
+        qblk.qblk_gemv_f32_noalloc(o.TYPE_Q4_K, wq, n, 4096, small, t.empty((1, n), device="cuda"))
+        ref = host(qblk.qblk_gemv_f32(o.TYPE_Q4_K, wq, n, k, x, y=y_eager))
+        y.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        got = host(y)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), rep
