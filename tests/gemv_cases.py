@@ -8,7 +8,9 @@ TYPES = [Q4_0, Q8_0, Q4_K, Q4_0_F16]
 
 # qblk_gemv against the oracle, every type: (n, k, batch)
 GEMV_RANDOM = [(37, 1024, 1), (300, 4096, 1), (129, 2304, 4), (64, 256, 8), (70, 512, 64),
-               (3100, 512, 2), (16400, 512, 5)]
+               (3100, 512, 2), (16400, 512, 5),
+               # a single row and two rows: one wave, most lanes past the last row
+               (1, 256, 1), (2, 512, 3)]
 
 # qblk_gemv with exact fp32 arithmetic, every type: batch (n = 67, k = 2304 / 2336)
 GEMV_EXACT_BATCH = [1, 3, 8, 11]

@@ -218,7 +218,9 @@ def test_gemv_random(wtype, n, k, batch):
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("m,n,k", [(1, 37, 256), (5, 300, 1024), (70, 129, 2304),
                                    (130, 257, 512), (256, 128, 4096), (16, 513, 2304),
-                                   (33, 100, 256), (64, 1000, 4096), (17, 47, 7168)])
+                                   (33, 100, 256), (64, 1000, 4096), (17, 47, 7168),
+                                   # one output, and rows long enough for many K steps
+                                   (1, 1, 256), (70, 65, 32768)])
 def test_gemm_random(wtype, m, n, k):
     print(f"gemm {TNAME[wtype]} m={m} n={n} k={k}", flush=True)
     rng = np.random.default_rng(41 * wtype + m + n)
