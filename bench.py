@@ -672,9 +672,23 @@ def gemm_bench(torch, qblk, synth, dev, iters, copies=16):
         "roofline": {"bound": "mfma", "kernel": "gemm_kernel<3>", "achieved": g["TOPS"],
                      "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                      "frac": round(g["TOPS"] / INT8_PEAK_TOPS, 4),
-                     "traffic": traffic_from_profile(GEMM_TRAFFIC, GEMM_SOURCES)},
+                     "traffic": traffic_from_profile(GEMM_TRAFFIC, GEMM_SOURCES),
+                     # the exact Q4_K scale step is two fp32 FMAs per (m, n, block):
+                     # at the non-packed fp32 rate that bounds the kernel first
+                     "valu_ceiling": valu_ceiling(512, 14336, 4096, g["us"])},
         "crossover": res,
     }
+
+
+FP32_FMA_PER_S = 256 * 4 * 16 * 2.4e9   # non-packed fp32 FMAs per second: CUs x SIMDs x lanes per cycle x clock
+
+
+def valu_ceiling(m, n, k, us):
+    """The time two fp32 FMAs per (m, n, 32-block) take at the chip's
+    non-packed fp32 FMA rate (the Q4_K GEMM's scale step), and the kernel's
+    fraction of it."""
+    t = 2 * m * n * (k // 32) / FP32_FMA_PER_S * 1e6
+    return {"fma_per_block_output": 2, "us": round(t, 2), "frac": round(t / us, 4)}
 
 
 def sym_bench(torch, qblk, synth, dev):
