@@ -95,8 +95,8 @@ constexpr bool gemv_stage_acts_in_lds(int b, int64_t nb) {
   return act_lds_bytes(b, static_cast<uint32_t>(nb)) <= (b == 1 ? kActLdsMax : kActLdsMaxBatch);
 }
 // Which GEMV kernel instance a product runs (pure host logic, no GPU):
-// gemv_kernel<type, b, r, u, sync, alds> or gemv_pipe_kernel<type, b, r,
-// fused, sync, alds>. mode: how the activation reaches the kernel.
+// gemv_kernel<type, b, r, u, sync, alds, waves> or gemv_pipe_kernel<type,
+// b, r, fused, sync, alds>. mode: how the activation reaches the kernel.
 enum : int { kGemvQuantized = 0, kGemvLdsFused = 1, kGemvInLaunch = 2 };
 struct GemvVariant {
   int type;

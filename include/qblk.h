@@ -17,8 +17,11 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers named w, x, y, wq, xq, sums are DEVICE pointers owned by the
- *     caller. The library never allocates, frees or synchronizes, and keeps
- *     no state between calls except a thread-local last HIP error code.
+ *     caller. The library never allocates, frees or synchronizes. Between
+ *     calls it keeps only a thread-local last HIP error code, the
+ *     thread-local handoff wait bound (qblk_gemv_f32_set_wait_limit), and,
+ *     for qblk_gemv_f32_noalloc, a fixed device array per GPU with its
+ *     address.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without waiting. Calls are reentrant and thread-safe.
  *   - Every argument is validated BEFORE anything is enqueued; on any error
@@ -280,7 +283,8 @@ qblk_status qblk_gemv_f32_noalloc(int type, const void *wq, int64_t n, int64_t k
  * that qblk_gemv (fused == 0) or qblk_gemv_f32 (fused != 0) launches for
  * this shape, for the first group of up to 8 activation rows, as the
  * kernel's template arguments: "gemv_kernel<type, rows, rows per wave,
- * chunks per step, in-launch quantization, activations in LDS>" or
+ * chunks per step, in-launch quantization, activations in LDS, waves per
+ * workgroup>" or
  * "gemv_pipe_kernel<type, rows, rows per wave, per-workgroup quantization,
  * in-launch quantization, activations in LDS>". Written NUL-terminated into
  * name[len]. Lets a test check that the instances a workload runs are the
