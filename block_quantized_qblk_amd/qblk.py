@@ -247,9 +247,12 @@ def qblk_gemv_f32_noalloc(wtype, wq, n, k, x, y, batch=None, stream=None):
     """qblk_gemv_f32 without a workspace (the library's fixed device array;
     allocates nothing, so y must be given). Calls that overlap on one GPU
     race on the array."""
+    import torch
     _require_cuda(wq, "wq")
     _require_cuda(x, "x", rows=True)
     _require_cuda(y, "y", rows=True)
+    if x.dtype != torch.float32 or y.dtype != torch.float32:
+        raise ValueError("x and y must be float32")
     if batch is None:
         batch = x.shape[0]
     if x.shape[1] < k or y.shape[0] < batch or y.shape[1] < n:

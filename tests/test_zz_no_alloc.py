@@ -88,3 +88,15 @@ def test_noalloc_in_a_graph():
         g.replay()
         got = host(y)
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), rep
+
+
+def test_noalloc_rejects_non_fp32_tensors():
+    print("gemv_f32_noalloc dtype checks", flush=True)
+    t = torch()
+    wq = t.zeros(qblk.qblk_weight_bytes(qblk.Q4_K, 64, 256), dtype=t.uint8, device="cuda")
+    x = t.zeros((1, 256), dtype=t.float16, device="cuda")
+    y = t.zeros((1, 64), dtype=t.float32, device="cuda")
+    with pytest.raises(ValueError):
+        qblk.qblk_gemv_f32_noalloc(qblk.Q4_K, wq, 64, 256, x, y)
+    with pytest.raises(ValueError):
+        qblk.qblk_gemv_f32_noalloc(qblk.Q4_K, wq, 64, 256, x.float(), y.half())
