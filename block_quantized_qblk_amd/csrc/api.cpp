@@ -30,6 +30,11 @@ bool valid_k(int t, int64_t k) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// a * b <= lim for a, b >= 0, decided without forming the product (sizes
+// come from the caller and may be arbitrarily large)
+bool mul_within(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= lim / a; }
+constexpr int64_t kMaxBytes = INT64_MAX;
+
 // A dispatch holds fewer than 2^32 work-items per grid dimension.
 constexpr int64_t kMaxGridThreads = (int64_t{1} << 32) - 256;
 
@@ -82,12 +87,13 @@ QBLK_EXPORT size_t qblk_weight_row_bytes(int type, int64_t k) {
 }
 
 QBLK_EXPORT size_t qblk_weight_bytes(int type, int64_t n, int64_t k) {
-  if (n < 0) return 0;
-  return static_cast<size_t>(n) * qblk_weight_row_bytes(type, k);
+  const int64_t rb = static_cast<int64_t>(qblk_weight_row_bytes(type, k));
+  if (n < 0 || !mul_within(n, rb, kMaxBytes)) return 0;
+  return static_cast<size_t>(n * rb);
 }
 
 QBLK_EXPORT size_t qblk_act_bytes(int64_t m, int64_t k) {
-  if (m < 0 || k <= 0 || k % 32 != 0) return 0;
+  if (m < 0 || k <= 0 || k % 32 != 0 || !mul_within(m, k, kMaxBytes / 2)) return 0;
   return static_cast<size_t>(m * k + 8 * m * (k / 32));
 }
 
@@ -99,7 +105,7 @@ QBLK_EXPORT qblk_status qblk_pack_weights(int type, const float* w, int64_t n, i
   if (w == nullptr || wq == nullptr) return QBLK_ERR_ARG;
   if (ldw < k) return QBLK_ERR_SHAPE;
   if (!aligned(w, 16) || ldw % 4 != 0 || !aligned(wq, 16)) return QBLK_ERR_ALIGN;
-  if (8 * n * (k / 32) > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  if (!mul_within(n, k / 32, kMaxGridThreads / 8)) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_pack_weights(type, w, n, k, ldw, wq, qblk::row_bytes(type, k), stream));
 }
@@ -112,7 +118,7 @@ QBLK_EXPORT qblk_status qblk_quantize_act(const float* x, int64_t m, int64_t k, 
   if (x == nullptr || xq == nullptr) return QBLK_ERR_ARG;
   if (ldx < k) return QBLK_ERR_SHAPE;
   if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(xq, 16)) return QBLK_ERR_ALIGN;
-  if (4 * m * (k / 32) > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  if (!mul_within(m, k / 32, kMaxGridThreads / 4)) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_quantize_act(x, m, k, ldx, xq, stream));
 }
@@ -122,7 +128,7 @@ QBLK_EXPORT qblk_status qblk_gemv(int type, const void* wq, int64_t n, int64_t k
   const qblk_status st = check_product(type, wq, n, k, xq, batch, y, ldy);
   if (st != QBLK_OK || n == 0 || batch == 0) return st;
   if (batch > QBLK_GEMV_MAX_BATCH) return QBLK_ERR_UNSUPPORTED;
-  if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  if (n > kMaxGridThreads / 64) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_gemv(type, wq, n, k, xq, batch, y, ldy, stream));
 }
@@ -147,7 +153,7 @@ QBLK_EXPORT qblk_status qblk_gemv_f32(int type, const void* wq, int64_t n, int64
   if (ldx < k) return QBLK_ERR_SHAPE;
   if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(work, 256)) return QBLK_ERR_ALIGN;
   if (batch > qblk::gemv_f32_max_batch(k)) return QBLK_ERR_UNSUPPORTED;
-  if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  if (n > kMaxGridThreads / 64) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_gemv_f32(type, wq, n, k, x, ldx, batch, y, ldy,
                                       qblk::gemv_work_in(work, batch, k), g_wait_ticks, stream));
@@ -163,7 +169,7 @@ QBLK_EXPORT qblk_status qblk_gemv_f32_noalloc(int type, const void* wq, int64_t 
   if (batch > qblk::gemv_f32_max_batch(k) || k > qblk::kNoallocMaxK ||
       static_cast<int64_t>(qblk_act_bytes(batch, k)) > qblk::kNoallocMaxActBytes)
     return QBLK_ERR_UNSUPPORTED;
-  if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  if (n > kMaxGridThreads / 64) return QBLK_ERR_UNSUPPORTED;
   qblk::GemvWork w{};
   const hipError_t e = qblk::gemv_scratch_work(stream, &w);
   if (e == hipErrorInvalidDevice) return QBLK_ERR_ARG;
@@ -205,10 +211,11 @@ QBLK_EXPORT qblk_status qblk_gemv_multi(int type, const qblk_gemv_desc* descs, i
     const qblk_gemv_desc& d = descs[i];
     const qblk_status st = check_product(type, d.wq, d.n, d.k, d.xq, batch, d.y, d.ldy);
     if (st != QBLK_OK) return st;
+    if (d.n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
     wgs += (d.n + 7) / 8;  // at most 2 rows per wave, 4 waves per workgroup
   }
   if (batch > QBLK_GEMV_MAX_BATCH) return QBLK_ERR_UNSUPPORTED;
-  if (256 * wgs > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  if (wgs > kMaxGridThreads / 256) return QBLK_ERR_UNSUPPORTED;
   qblk::GemvDesc d[QBLK_GEMV_MULTI_MAX];
   for (int i = 0; i < count; ++i)
     d[i] = qblk::GemvDesc{descs[i].wq, descs[i].n, descs[i].k, descs[i].xq, descs[i].y, descs[i].ldy};
@@ -224,7 +231,7 @@ QBLK_EXPORT qblk_status qblk_gemv_float(int type, const void* wq, int64_t n, int
   if (ldx < k) return QBLK_ERR_SHAPE;
   if (ldx % 4 != 0) return QBLK_ERR_ALIGN;
   if (batch > QBLK_GEMV_MAX_BATCH) return QBLK_ERR_UNSUPPORTED;
-  if (64 * n > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  if (n > kMaxGridThreads / 64) return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_gemv_float(type, wq, n, k, x, ldx, batch, y, ldy, stream));
 }
@@ -237,7 +244,7 @@ QBLK_EXPORT qblk_status qblk_gemm(int type, const void* wq, int64_t n, int64_t k
   // or, for m <= 64, x = n / 64; a workgroup addresses its activation and
   // weight rows with 32-bit offsets, so k is limited to 2^24
   const int64_t wgs = m <= qblk::kGemmSmallMaxRows ? (n + 63) / 64 : (n + 127) / 128;
-  if (256 * wgs > kMaxGridThreads || (m + 127) / 128 > 65535 || k > kMaxGemmK)
+  if (wgs > kMaxGridThreads / 256 || (m + 127) / 128 > 65535 || k > kMaxGemmK)
     return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_gemm(type, wq, n, k, xq, m, y, ldy, stream));
@@ -254,7 +261,9 @@ bool valid_kv(int type, int64_t head_dim) {
 
 QBLK_EXPORT size_t qblk_kv_cache_bytes(int type, int64_t n_kv, int64_t n_ctx, int64_t head_dim) {
   if (!valid_kv(type, head_dim) || n_kv <= 0 || n_ctx <= 0 || n_kv > 65535) return 0;
-  return static_cast<size_t>(n_kv * n_ctx * qblk::row_bytes(type, head_dim));
+  const int64_t head_bytes = n_kv * qblk::row_bytes(type, head_dim);  // < 2^25
+  if (!mul_within(n_ctx, head_bytes, kMaxBytes)) return 0;
+  return static_cast<size_t>(n_ctx * head_bytes);
 }
 
 QBLK_EXPORT qblk_status qblk_kv_store(int type, const float* x, int64_t n_kv, int64_t head_dim, int64_t ldx,
@@ -265,7 +274,7 @@ QBLK_EXPORT qblk_status qblk_kv_store(int type, const float* x, int64_t n_kv, in
   if (x == nullptr || cache == nullptr) return QBLK_ERR_ARG;
   if (ldx < head_dim) return QBLK_ERR_SHAPE;
   if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(cache, 16)) return QBLK_ERR_ALIGN;
-  if (n_kv > 65535) return QBLK_ERR_UNSUPPORTED;
+  if (n_kv > 65535 || qblk_kv_cache_bytes(type, n_kv, n_ctx, head_dim) == 0) return QBLK_ERR_UNSUPPORTED;
   const int64_t rb = qblk::row_bytes(type, head_dim);
   (void)hipGetLastError();
   return finish(qblk::launch_pack_weights(type, x, n_kv, head_dim, ldx, static_cast<uint8_t*>(cache) + pos * rb,
@@ -282,7 +291,8 @@ QBLK_EXPORT qblk_status qblk_kv_scores(int type, const void* cache, int64_t n_kv
   if (cache == nullptr || q == nullptr || scores == nullptr) return QBLK_ERR_ARG;
   if (lds < n_tok) return QBLK_ERR_SHAPE;
   if (!aligned(cache, 16) || !aligned(q, 16) || !aligned(scores, 4)) return QBLK_ERR_ALIGN;
-  if (n_head / n_kv > 8 || n_kv > 65535) return QBLK_ERR_UNSUPPORTED;
+  if (n_head / n_kv > 8 || n_kv > 65535 || qblk_kv_cache_bytes(type, n_kv, n_ctx, head_dim) == 0)
+    return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_kv_scores(type, cache, n_kv, n_ctx, n_tok, head_dim, q, n_head, scores, lds, stream));
 }
@@ -291,7 +301,8 @@ QBLK_EXPORT qblk_status qblk_block_sums(int type, const void* wq, int64_t n, int
                                 int64_t m, int32_t* sums, hipStream_t stream) {
   const qblk_status st = check_product(type, wq, n, k, xq, m, sums, n);
   if (st != QBLK_OK || n == 0 || m == 0) return st;
-  if (m * n * (k / 32) > kMaxGridThreads) return QBLK_ERR_UNSUPPORTED;
+  if (!mul_within(m, n, kMaxGridThreads) || !mul_within(m * n, k / 32, kMaxGridThreads))
+    return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(qblk::launch_block_sums(type, wq, n, k, xq, m, sums, stream));
 }

@@ -280,3 +280,27 @@ def test_gemv_f32_fallback_counter_location():
     assert qblk.qblk_gemv_f32_fallback_offset(1, 100) == 0
     assert qblk.lib().qblk_gemv_f32_set_wait_limit(0) == OK
     assert qblk.lib().qblk_gemv_f32_set_wait_limit(-1) == OK
+
+
+def test_huge_sizes_are_rejected_without_overflow():
+    """Sizes whose byte counts or grids would overflow 64-bit arithmetic are
+    reported as invalid or unsupported (the sanitizer run of these tests
+    halts on any signed overflow in the checks themselves)."""
+    lib = qblk.lib()
+    big, huge = 1 << 40, 1 << 62
+    assert qblk.qblk_act_bytes(big, 1 << 20) == (1 << 60) + (1 << 58)   # still representable
+    assert qblk.qblk_act_bytes(huge, 1 << 20) == 0
+    assert qblk.qblk_weight_bytes(o.TYPE_Q8_0, huge, 1 << 20) == 0
+    assert qblk.qblk_kv_cache_bytes(o.TYPE_Q8_0, 8, huge, 128) == 0
+    w, x, y = _p(FAKE), _p(FAKE + 0x100000), _p(FAKE + 0x200000)
+    for n in (big, huge):
+        assert lib.qblk_pack_weights(2, x, n, 4096, 4096, w, NULL) == ERR_UNSUPPORTED
+        assert lib.qblk_gemv(3, w, n, 256, x, 1, y, n, NULL) == ERR_UNSUPPORTED
+        assert lib.qblk_gemv_float(3, w, n, 256, x, 256, 1, y, n, NULL) == ERR_UNSUPPORTED
+        assert lib.qblk_gemm(3, w, n, 256, x, 512, y, n, NULL) == ERR_UNSUPPORTED
+        assert lib.qblk_block_sums(3, w, n, 256, x, n, _p(FAKE), NULL) == ERR_UNSUPPORTED
+        assert lib.qblk_quantize_act(x, n, 4096, 4096, w, NULL) == ERR_UNSUPPORTED
+    work = _p(FAKE + 0x400000)
+    assert lib.qblk_gemv_f32(3, w, huge, 256, x, 256, 1, y, huge, work, NULL) == ERR_UNSUPPORTED
+    assert lib.qblk_kv_store(2, x, 8, 128, 128, w, huge, 0, NULL) == ERR_UNSUPPORTED
+    assert lib.qblk_kv_scores(2, w, 8, huge, 16, 128, x, 64, y, 16, NULL) == ERR_UNSUPPORTED
