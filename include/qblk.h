@@ -154,6 +154,8 @@ qblk_status qblk_pack_weights(int type, const float *w, int64_t n, int64_t k,
  * per row and per 32 consecutive elements: d = max|x| / 127 (IEEE fp32
  * division), q = round_half_away(x / d) (IEEE fp32 division), d == 0 gives
  * q == 0; the int32 sum of the 32 codes is stored beside d.
+ * Inputs must be finite: a block holding an infinity or a NaN gets
+ * unspecified codes and scale (the other blocks are quantized as usual).
  *   x  : fp32 [m][ldx].
  *   xq : out, qblk_act_bytes(m, k) bytes, layout above.
  * Errors: QBLK_ERR_ARG, QBLK_ERR_SHAPE (k % 32 != 0, k <= 0, ldx < k),
