@@ -397,6 +397,197 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   gemv_body<TYPE, B, R, U, SYNC, ALDS, WAVES>(g, blockIdx.x);
 }
 
+// ---------------------------------------------------------------- matrix-core form, 3-4 activation rows
+// Q4_K with 3 or 4 activation rows and k a multiple of 2048. The dot4 form
+// spends 73 VALU instructions per row and block at 4 rows (32 of them
+// dot4); here each block's integer dots run on v_mfma_i32_16x16x64_i8 and
+// the VALU keeps the unpack, the scale decode and the scale FMAs (about 40).
+//
+// Operands (D = A x B, 16 x 16, K = 64): B holds 16 weight rows (column i =
+// lane & 15), its k-group q = lane >> 4 holds half of block 4u + q of the
+// step (two MFMAs per block pair of halves). A row m = 4 b + a (activation
+// row a, block b of the step) is nonzero only in k-group b, so output
+// D[4 q + a][i] is the integer dot of weight row i with activation row a
+// over one whole block: lane (i, q) ends with the four activation rows of its
+// own row and block, whose scales it decoded itself. A quarter of the MFMA
+// work is useful; the matrix cores have that to spare.
+//
+// Data movement: that operand layout needs 16 rows per load, and 16-row
+// loads of 64 bytes each stream at about two thirds of the bandwidth of the
+// per-row KiB loads (a stream probe over the 70B gate/up: 4.4 against 6.4
+// TB/s). So a workgroup owns one 16-row tile, and each 64-block chunk of its
+// 16 rows (1 KiB per row, the row's headers, and the chunk's activation
+// codes and scale pairs) moves by direct global-to-LDS loads into one of two
+// LDS stages while the other is computed. Row r's lane l fetches block
+// l ^ (r & 15) of the chunk, which keeps every load a whole KiB and makes the
+// transposed operand reads conflict-free. The four waves take 16 blocks of a
+// chunk each; their sums meet in LDS at the end in wave order. The direct
+// loads are issued by inline assembly with explicit waits: the compiler does
+// not track them, and with its own waits every LDS read would drain the
+// ring. Nothing else in the loop touches vector memory.
+constexpr uint32_t kRingW = 16384;   // 16 rows x 1 KiB of codes
+constexpr uint32_t kRingH = 2048;    // 16 rows x 128 B of headers
+constexpr uint32_t kRingA = 8192;    // 4 activation rows x 2 KiB of codes
+constexpr uint32_t kRingD = 2048;    // 4 activation rows x 64 (d, sum) pairs
+constexpr uint32_t kRingStage = kRingW + kRingH + kRingA + kRingD;
+constexpr uint32_t kRingZero = 512;  // zero operand slots of the unused A lanes
+constexpr uint32_t kRingLds = 2 * kRingStage + kRingZero;
+constexpr int kRingDma = 10;         // direct loads per wave and stage
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 (or 4) bytes per lane from global memory into LDS at lds + 16 l (4 l);
+// lds must be wave-uniform. m0 is not otherwise used by this kernel; the
+// clobber tells the compiler it changes.
+__device__ __forceinline__ void ring_dma16(const uint8_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void ring_dma4(const uint8_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// s_waitcnt: at most n vector-memory operations of the wave outstanding, and
+// all of its LDS operations complete (a barrier after it publishes the
+// wave's LDS writes)
+constexpr int ring_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
+
+template <int B, bool SYNC>
+__global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
+  static_assert(B >= 1 && B <= 4, "one activation row per wave");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+  const uint32_t k = g.nb * 32u;
+  const uint32_t nc = g.nb >> 6;  // the launcher guarantees nb % 64 == 0
+  uint64_t tag = 0;
+  if constexpr (SYNC) {
+    tag = launch_tag();
+    produce<B>(g, tag);
+  }
+  // per-lane sources: this wave's 4 weight rows (block lane ^ row of each
+  // chunk), 2 x 2 rows of headers (4 bytes per lane), and activation row wv
+  const uint8_t* wsrc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t ri = 4 * wv + r;
+    const int64_t row = row0 + ri < g.n ? row0 + ri : g.n - 1;
+    wsrc[r] = g.w + row * g.row_bytes + g.hdr_bytes + 16u * (lane ^ ri);
+  }
+  const uint8_t* hsrc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t rr = row0 + 4 * wv + 2 * h + (lane >> 5);
+    hsrc[h] = g.w + (rr < g.n ? rr : g.n - 1) * g.row_bytes + 4u * (lane & 31u);
+  }
+  const uint32_t arow = wv < static_cast<uint32_t>(B) ? wv : B - 1;
+  const uint8_t* asrc = g.aq + arow * k + 16u * lane;
+  const uint8_t* dsrc = g.ads + 8u * (arow * g.nb) + 4u * lane;
+  auto issue_weights = [&](uint32_t c, uint32_t st) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      ring_dma16(wsrc[r] + 1024u * c, __builtin_amdgcn_readfirstlane(st + (4 * wv + r) * 1024u));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ring_dma4(hsrc[h] + 128u * c, __builtin_amdgcn_readfirstlane(st + kRingW + wv * 512u + h * 256u));
+  };
+  auto issue_acts = [&](uint32_t c, uint32_t st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ring_dma16(asrc + 2048u * c + 1024u * h,
+                 __builtin_amdgcn_readfirstlane(st + kRingW + kRingH + wv * 2048u + h * 1024u));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ring_dma4(dsrc + 512u * c + 256u * h,
+                __builtin_amdgcn_readfirstlane(st + kRingW + kRingH + kRingA + wv * 512u + h * 256u));
+  };
+  for (uint32_t e = threadIdx.x; e < kRingZero / 16; e += 256u)
+    *reinterpret_cast<uint4*>(smem + 2 * kRingStage + 16u * e) = make_uint4(0, 0, 0, 0);
+  issue_weights(0, lds0);  // in flight while the activation is awaited
+  if constexpr (SYNC) wait_slices<B>(g, tag);
+  issue_acts(0, lds0);
+
+  // per-lane LDS read addresses
+  const uint32_t i = lane & 15u, q = lane >> 4;  // weight row (B column), k-group
+  const uint32_t aa = lane & 3u, ab = (lane & 15u) >> 2;
+  const bool anz = ab == q && aa < static_cast<uint32_t>(B);
+  // A operand: activation row aa, block 16 wv + 4 u + ab, bytes [16 h, 16 h + 16); other lanes read zeros
+  const uint32_t a_base = anz ? kRingW + kRingH + aa * 2048u + (16u * wv + ab) * 32u : 2 * kRingStage;
+  const uint32_t a_stage = anz ? kRingStage : 0u;
+  const uint32_t h_base = kRingW + (i >> 2) * 512u + (i & 3u) * 128u + 32u * wv;  // + 16 (u >> 1)
+  const uint32_t d_base = kRingW + kRingH + kRingA + (16u * wv + q) * 8u;        // + 512 a + 32 u
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  v4i cinit;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) cinit[v] = kMagicBits;
+  const uint32_t msk = 0x0F0F0F0Fu;
+  float acc[B];
+#pragma unroll
+  for (int a = 0; a < B; ++a) acc[a] = 0.0f;
+
+  for (uint32_t c = 0; c < nc; ++c) {
+    __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));  // this wave's loads of stage c are in LDS
+    __syncthreads();                               // everyone's; stage c + 1's buffer is free
+    const uint32_t cur = (c & 1u) * kRingStage;
+    if (c + 1 < nc) {
+      const uint32_t nxt = lds0 + ((c + 1) & 1u) * kRingStage;
+      issue_weights(c + 1, nxt);
+      issue_acts(c + 1, nxt);
+    }
+    const uint8_t* ap = smem + a_base + (c & 1u) * a_stage;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t b = 16u * wv + 4u * u + q;  // this lane's block of the chunk
+      const uint4 w = *reinterpret_cast<const uint4*>(smem + cur + i * 1024u + 16u * (b ^ i));
+      const v4i a0 = *reinterpret_cast<const v4i*>(ap + 128u * u);
+      const v4i a1 = *reinterpret_cast<const v4i*>(ap + 128u * u + 16u);
+      // the unpack order of dot_nib32: low, then high nibbles of each dword
+      v4i w0, w1;
+      w0[0] = w.x & msk; w0[1] = (w.x >> 4) & msk; w0[2] = w.y & msk; w0[3] = (w.y >> 4) & msk;
+      w1[0] = w.z & msk; w1[1] = (w.z >> 4) & msk; w1[2] = w.w & msk; w1[3] = (w.w >> 4) & msk;
+      v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, w0, cinit, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, w1, d, 0, 0, 0);  // 1.5 * 2^23 + S per activation row
+      const uint4 hd = *reinterpret_cast<const uint4*>(smem + cur + h_base + 16u * (u >> 1));
+      const int j = static_cast<int>((4u * u + q) & 7u);
+      const float sw = half_bits_to_float(hd.x) * static_cast<float>(q4k_sc(hd, j));
+      const float wm = half_bits_to_float(hd.x >> 16) * static_cast<float>(q4k_mn(hd, j));
+      const float ncs = -kMagic * sw;
+#pragma unroll
+      for (int a = 0; a < B; ++a) {
+        const float2 ds = *reinterpret_cast<const float2*>(smem + cur + d_base + a * 512u + 32u * u);
+        const float t = fmaf(__int_as_float(d[a]), sw, ncs);                    // S * d * sc_j, exact
+        const float t2 = fmaf(wm, static_cast<float>(__float_as_int(ds.y)), t);  // + d_min * mn_j * A
+        acc[a] = fmaf(t2, ds.x, acc[a]);
+      }
+    }
+  }
+  // the 4 k-groups of a wave, then the 4 waves, in a fixed order
+#pragma unroll
+  for (int a = 0; a < B; ++a) {
+    float v = acc[a];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    acc[a] = v;
+  }
+  __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));
+  __syncthreads();  // every wave is done with the stages
+  float* part = reinterpret_cast<float*>(smem);  // [4 waves][4][16]
+  if (lane < 16) {
+#pragma unroll
+    for (int a = 0; a < B; ++a) part[(wv * 4 + a) * 16 + lane] = acc[a];
+  }
+  __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));
+  __syncthreads();
+  if (wv == 0 && lane < 16u * B) {
+    const uint32_t a = lane >> 4, r = lane & 15u;
+    const float v = ((part[a * 16 + r] + part[(4 + a) * 16 + r]) + part[(8 + a) * 16 + r]) + part[(12 + a) * 16 + r];
+    if (row0 + r < g.n) g.y[a * g.ldy + row0 + r] = v;
+  }
+}
+
 // Several independent products in one launch (a descriptor list, e.g. the
 // q, k and v matrices of a layer kept as separate buffers): the workgroups
 // of descriptor i are [first[i], first[i+1]) and run the classic kernel on
@@ -619,6 +810,20 @@ hipError_t launch_cfg(const Plan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The matrix-core kernel: one 16-row tile per workgroup (Q4_K, 3-4 rows,
+// k a multiple of 2048; select_gemv only picks it there).
+template <int TYPE, int B, bool SYNC>
+hipError_t launch_ring(const Plan& p, hipStream_t s) {
+  if constexpr (TYPE == kQ4_K && B >= 3 && B <= 4) {
+    if (p.nb % 64 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_ring_kernel<B, SYNC>), dim3(static_cast<uint32_t>((p.n + 15) / 16)), dim3(256),
+                       kRingLds, s, make_args(p));
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 // How the activation reaches the kernel.
 enum Mode { kQuantized = kGemvQuantized, kLdsFused = kGemvLdsFused, kInLaunch = kGemvInLaunch };
 
@@ -639,6 +844,7 @@ hipError_t launch_b(const Plan& p, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   } else {
+    if (v.ring) return launch_ring<TYPE, B, SYNC>(p, s);
     if (v.waves == 8) {
       if (ru == 81) return launch_cfg<TYPE, B, 8, 1, SYNC, 8>(p, s);
       if (ru == 41) return launch_cfg<TYPE, B, 4, 1, SYNC, 8>(p, s);

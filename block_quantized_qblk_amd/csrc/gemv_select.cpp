@@ -25,6 +25,16 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
   v.sync = mode == kGemvInLaunch;
   v.fused = mode == kGemvLdsFused;
   const int64_t nb = k / 32;
+  // Q4_K at 3-4 activation rows with whole 2048-element chunks: the
+  // matrix-core kernel with the direct-load LDS ring (gemv_ring_kernel).
+  // Measured against the dot4 kernels on a quantized activation: at 4 rows
+  // faster on every 70B- and 7B-shaped matrix (70B layer 103 against 118 us;
+  // down 25.6 against 33.7 us), at 3 rows on all but the 7B q/k/v (6.07
+  // against 6.06 us); at 2 rows faster on only 2 of 8, so not used there.
+  if (type == kQ4_K && (b == 3 || b == 4) && k % 2048 == 0) {
+    v.ring = true;
+    return v;
+  }
   if (mode == kGemvLdsFused) {
     v.pipe = true;
     v.r = n >= 8192 ? 4 : 2;
@@ -81,6 +91,7 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len) {
   const char* t = v.sync ? "true" : "false";
   const char* a = v.alds ? "true" : "false";
+  if (v.ring) return snprintf(buf, len, "gemv_ring_kernel<%d, %s>", v.b, t);
   if (v.pipe)
     return snprintf(buf, len, "gemv_pipe_kernel<%d, %d, %d, %s, %s, %s>", v.type, v.b, v.r,
                     v.fused ? "true" : "false", t, a);

@@ -95,8 +95,9 @@ constexpr bool gemv_stage_acts_in_lds(int b, int64_t nb) {
   return act_lds_bytes(b, static_cast<uint32_t>(nb)) <= (b == 1 ? kActLdsMax : kActLdsMaxBatch);
 }
 // Which GEMV kernel instance a product runs (pure host logic, no GPU):
-// gemv_kernel<type, b, r, u, sync, alds, waves> or gemv_pipe_kernel<type,
-// b, r, fused, sync, alds>. mode: how the activation reaches the kernel.
+// gemv_kernel<type, b, r, u, sync, alds, waves>, gemv_pipe_kernel<type,
+// b, r, fused, sync, alds> or gemv_ring_kernel<b, sync>. mode: how the
+// activation reaches the kernel.
 enum : int { kGemvQuantized = 0, kGemvLdsFused = 1, kGemvInLaunch = 2 };
 struct GemvVariant {
   int type;
@@ -108,6 +109,7 @@ struct GemvVariant {
   bool alds;  // activation rows staged in LDS
   bool fused; // activation quantized in every workgroup's LDS
   int waves;  // waves per workgroup (classic kernel)
+  bool ring;  // gemv_ring_kernel (Q4_K, 3-4 rows: matrix cores, direct-load LDS ring)
 };
 GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode);
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len);

@@ -194,7 +194,11 @@ qblk_status qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void
  *   rows of k;  y : fp32 [batch][ldy].
  * The descriptors are read on the host during the call (the array need not
  * outlive it); their outputs must not overlap. Results are bit-identical to
- * qblk_gemv on each descriptor. Descriptors with n == 0 are skipped.
+ * qblk_gemv on each descriptor, except where qblk_gemv runs the matrix-core
+ * kernel (Q4_K with 3 or 4 activation rows and k a multiple of 2048;
+ * qblk_gemv_variant names it gemv_ring_kernel): there the same block
+ * products and scale steps are summed in another fp32 order. Descriptors
+ * with n == 0 are skipped.
  * Errors: QBLK_ERR_ARG (type, count < 0, null descs), the qblk_gemv errors of
  * any descriptor, QBLK_ERR_UNSUPPORTED (count > QBLK_GEMV_MULTI_MAX, batch >
  * QBLK_GEMV_MAX_BATCH).
@@ -286,7 +290,8 @@ qblk_status qblk_gemv_f32_noalloc(int type, const void *wq, int64_t n, int64_t k
  * this shape, for the first group of up to 8 activation rows, as the
  * kernel's template arguments: "gemv_kernel<type, rows, rows per wave,
  * chunks per step, in-launch quantization, activations in LDS, waves per
- * workgroup>" or
+ * workgroup>", "gemv_ring_kernel<rows, in-launch quantization>" (Q4_K with 3
+ * or 4 rows and k a multiple of 2048: matrix cores) or
  * "gemv_pipe_kernel<type, rows, rows per wave, per-workgroup quantization,
  * in-launch quantization, activations in LDS>". Written NUL-terminated into
  * name[len]. Lets a test check that the instances a workload runs are the

@@ -10,7 +10,13 @@ TYPES = [Q4_0, Q8_0, Q4_K, Q4_0_F16]
 GEMV_RANDOM = [(37, 1024, 1), (300, 4096, 1), (129, 2304, 4), (64, 256, 8), (70, 512, 64),
                (3100, 512, 2), (16400, 512, 5),
                # a single row and two rows: one wave, most lanes past the last row
-               (1, 256, 1), (2, 512, 3)]
+               (1, 256, 1), (2, 512, 3),
+               # Q4_K's matrix-core kernel (3-4 rows, k a multiple of 2048): one
+               # 2048-element chunk with a ragged last tile, and fewer rows than a tile
+               (1000, 2048, 3), (5, 4096, 4)]
+
+# Q4_K's matrix-core kernel with exact fp32 arithmetic: (n, k, batch)
+GEMV_RING_EXACT = [(67, 4096, 3), (67, 4096, 4), (16, 2048, 4)]
 
 # qblk_gemv with exact fp32 arithmetic, every type: batch (n = 67, k = 2304 / 2336)
 GEMV_EXACT_BATCH = [1, 3, 8, 11]
@@ -71,6 +77,9 @@ def covered():
                 out.add((t, n, k, b, False))
         for b in GEMV_EXACT_BATCH:
             out.add((t, 67, 2304 if t == Q4_K else 2336, b, False))
+    for n, k, b in GEMV_RING_EXACT:
+        out.add((Q4_K, n, k, b, False))
+    for t in TYPES:
         for n, k, b in GEMV_F32 + GEMV_F32_IN_LAUNCH:
             if t != Q4_K or k % 256 == 0:
                 out.add((t, n, k, b, True))
