@@ -420,7 +420,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
 // codes and scale pairs) moves by direct global-to-LDS loads into one of two
 // LDS stages while the other is computed. Row r's lane l fetches block
 // l ^ (r & 15) of the chunk, which keeps every load a whole KiB and makes the
-// transposed operand reads conflict-free. The four waves take 16 blocks of a
+// transposed operand reads conflict-free. The headers and activation units
+// are permuted the same way (each lane fetches the unit that its LDS slot
+// should hold): row r's header of super-block s sits at unit s ^ ((r >> 1) &
+// 7), and activation slot a's 16-B unit U at U ^ ((a & 1) | (a & 2) << 2), so
+// that the 16 lanes of each read hit 16 different bank groups (with the
+// plain layouts, bank conflicts took about half of the LDS cycles; the 70B
+// q/k/v at 4 rows went from 15.8 to 15.1 us). The four waves take 16 blocks of a
 // chunk each; their sums meet in LDS at the end in wave order. The direct
 // loads are issued by inline assembly with explicit waits: the compiler does
 // not track them, and with its own waits every LDS read would drain the
@@ -432,6 +438,7 @@ constexpr uint32_t kRingD = 2048;    // 4 activation rows x 64 (d, sum) pairs
 constexpr uint32_t kRingStage = kRingW + kRingH + kRingA + kRingD;
 constexpr uint32_t kRingZero = 512;  // zero operand slots of the unused A lanes
 constexpr uint32_t kRingLds = 2 * kRingStage + kRingZero;
+constexpr uint32_t kRingTilesLds = kRingLds + 2048;  // + the partial sums of two tiles, [2][4][4][16]
 constexpr int kRingDma = 10;         // direct loads per wave and stage
 
 #pragma clang diagnostic push
@@ -465,6 +472,139 @@ __device__ __forceinline__ void ring_dma4_nt(const uint8_t* src, uint32_t lds) {
 // wave's LDS writes)
 constexpr int ring_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
 
+// Direct-load sources of one 16-row tile (first row row0) for this wave: its 4
+// weight rows (row r's lane l fetches block l ^ r of each chunk) and 2 x 2
+// rows of headers, 4 bytes per lane, row r's 16-B header of super-block sb
+// fetched into unit sb ^ ((r >> 1) & 7) of the row's 128 B ((r >> 1) & 7 is
+// 2 wv + h for this wave's header rows). Rows past the end repeat the last.
+struct RingSrc {
+  const uint8_t* w[4];
+  const uint8_t* h[2];
+};
+__device__ __forceinline__ RingSrc ring_tile_src(const GemvArgs& g, int64_t row0, uint32_t lane, uint32_t wv) {
+  RingSrc src;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t ri = 4 * wv + r;
+    const int64_t row = row0 + ri < g.n ? row0 + ri : g.n - 1;
+    src.w[r] = g.w + row * g.row_bytes + g.hdr_bytes + 16u * (lane ^ ri);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t rr = row0 + 4 * wv + 2 * h + (lane >> 5);
+    src.h[h] = g.w + (rr < g.n ? rr : g.n - 1) * g.row_bytes + 16u * (((lane & 31u) >> 2) ^ (2 * wv + h)) +
+               4u * (lane & 3u);
+  }
+  return src;
+}
+// chunk c of the tile's weights and headers into the stage at LDS address st
+__device__ __forceinline__ void ring_issue_weights(const RingSrc& src, uint32_t c, uint32_t st, uint32_t wv) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    ring_dma16_nt(src.w[r] + 1024u * c, __builtin_amdgcn_readfirstlane(st + (4 * wv + r) * 1024u));
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    ring_dma4_nt(src.h[h] + 128u * c, __builtin_amdgcn_readfirstlane(st + kRingW + wv * 512u + h * 256u));
+}
+// chunk c of activation row min(wv, B - 1): its codes, 16-B unit U fetched into
+// unit U ^ ((wv & 1) | (wv & 2) << 2) of slot wv, and its (d, sum) pairs
+struct RingAct {
+  const uint8_t* a;
+  const uint8_t* d;
+};
+template <int B>
+__device__ __forceinline__ RingAct ring_act_src(const GemvArgs& g, uint32_t lane, uint32_t wv) {
+  const uint32_t arow = wv < static_cast<uint32_t>(B) ? wv : B - 1;
+  const uint32_t asw = (wv & 1u) | ((wv & 2u) << 2);
+  return RingAct{g.aq + arow * g.nb * 32u + 16u * (lane ^ asw), g.ads + 8u * (arow * g.nb) + 4u * lane};
+}
+__device__ __forceinline__ void ring_issue_acts(const RingAct& src, uint32_t c, uint32_t st, uint32_t wv) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    ring_dma16(src.a + 2048u * c + 1024u * h,
+               __builtin_amdgcn_readfirstlane(st + kRingW + kRingH + wv * 2048u + h * 1024u));
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    ring_dma4(src.d + 512u * c + 256u * h,
+              __builtin_amdgcn_readfirstlane(st + kRingW + kRingH + kRingA + wv * 512u + h * 256u));
+}
+
+// Per-lane LDS read addresses of a stage (relative to the stage).
+struct RingLane {
+  uint32_t w_row;       // weight row i's KiB
+  uint32_t w_blk;       // 16 wv + q: the lane's block at u = 0 (+ 4 u), XORed with i
+  uint32_t i;
+  uint32_t a_base[2][2];  // A operand [u & 1][half] (+ 256 (u >> 1)); zero lanes: the zero slots
+  uint32_t a_stage;       // stage stride of the A reads (0 for the zero lanes)
+  uint32_t h_base[2];     // row i's header of super-block 2 wv + (u >> 1)
+  uint32_t d_base;        // (d, sum) of block 16 wv + q of activation row 0 (+ 512 a + 32 u)
+  uint32_t q;
+};
+template <int B>
+__device__ __forceinline__ RingLane ring_lane(uint32_t lane, uint32_t wv) {
+  RingLane L;
+  const uint32_t i = lane & 15u, q = lane >> 4;  // weight row (B column), k-group
+  const uint32_t aa = lane & 3u, ab = (lane & 15u) >> 2;
+  // A operand: activation row aa, block 16 wv + 4 u + ab, bytes [16 h, 16 h + 16), unit
+  // 32 wv + 8 u + 2 q + h swizzled as the loads placed it; the lanes outside row ab == q
+  // of their k-group read zeros, from a slot that the active lanes of that k-group leave free
+  const bool anz = ab == q && aa < static_cast<uint32_t>(B);
+#pragma unroll
+  for (int uo = 0; uo < 2; ++uo)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      L.a_base[uo][hh] = anz ? kRingW + kRingH + aa * 2048u +
+                                   16u * (32u * wv + 8u * (uo ^ (aa >> 1)) + 2u * q + (hh ^ (aa & 1u)))
+                             : 2 * kRingStage + 16u * (2u * q + 4u);
+  L.a_stage = anz ? kRingStage : 0u;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) L.h_base[t] = kRingW + 128u * i + 16u * ((2u * wv + t) ^ ((i >> 1) & 7u));
+  L.d_base = kRingW + kRingH + kRingA + (16u * wv + q) * 8u;
+  L.w_row = i * 1024u;
+  L.w_blk = 16u * wv + q;
+  L.i = i;
+  L.q = q;
+  return L;
+}
+
+// The stage at LDS offset cur (A reads at + ast): 4 steps of 2 MFMAs, each
+// followed by this lane's scale steps for its (row, block).
+template <int B>
+__device__ __forceinline__ void ring_chunk(const uint8_t* smem, uint32_t cur, uint32_t ast, const RingLane& L,
+                                           float (&acc)[B]) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  v4i cinit;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) cinit[v] = kMagicBits;
+  const uint32_t msk = 0x0F0F0F0Fu;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t b = L.w_blk + 4u * u;  // this lane's block of the chunk
+    const uint4 w = *reinterpret_cast<const uint4*>(smem + cur + L.w_row + 16u * (b ^ L.i));
+    const v4i a0 = *reinterpret_cast<const v4i*>(smem + L.a_base[u & 1][0] + ast + 256u * (u >> 1));
+    const v4i a1 = *reinterpret_cast<const v4i*>(smem + L.a_base[u & 1][1] + ast + 256u * (u >> 1));
+    // the unpack order of dot_nib32: low, then high nibbles of each dword
+    v4i w0, w1;
+    w0[0] = w.x & msk; w0[1] = (w.x >> 4) & msk; w0[2] = w.y & msk; w0[3] = (w.y >> 4) & msk;
+    w1[0] = w.z & msk; w1[1] = (w.z >> 4) & msk; w1[2] = w.w & msk; w1[3] = (w.w >> 4) & msk;
+    v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, w0, cinit, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, w1, d, 0, 0, 0);  // 1.5 * 2^23 + S per activation row
+    const uint4 hd = *reinterpret_cast<const uint4*>(smem + cur + L.h_base[u >> 1]);
+    const int j = static_cast<int>((4u * u + L.q) & 7u);
+    const float sw = half_bits_to_float(hd.x) * static_cast<float>(q4k_sc(hd, j));
+    const float wm = half_bits_to_float(hd.x >> 16) * static_cast<float>(q4k_mn(hd, j));
+    const float ncs = -kMagic * sw;
+#pragma unroll
+    for (int a = 0; a < B; ++a) {
+      const float2 ds = *reinterpret_cast<const float2*>(smem + cur + L.d_base + a * 512u + 32u * u);
+      const float t = fmaf(__int_as_float(d[a]), sw, ncs);                    // S * d * sc_j, exact
+      const float t2 = fmaf(wm, static_cast<float>(__float_as_int(ds.y)), t);  // + d_min * mn_j * A
+      acc[a] = fmaf(t2, ds.x, acc[a]);
+    }
+  }
+}
+
+// One 16-row tile per workgroup (grid = tiles).
 template <int B, bool SYNC>
 __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
   static_assert(B >= 1 && B <= 4, "one activation row per wave");
@@ -473,69 +613,21 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-  const uint32_t k = g.nb * 32u;
   const uint32_t nc = g.nb >> 6;  // the launcher guarantees nb % 64 == 0
   uint64_t tag = 0;
   if constexpr (SYNC) {
     tag = launch_tag();
     produce<B>(g, tag);
   }
-  // per-lane sources: this wave's 4 weight rows (block lane ^ row of each
-  // chunk), 2 x 2 rows of headers (4 bytes per lane), and activation row wv
-  const uint8_t* wsrc[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t ri = 4 * wv + r;
-    const int64_t row = row0 + ri < g.n ? row0 + ri : g.n - 1;
-    wsrc[r] = g.w + row * g.row_bytes + g.hdr_bytes + 16u * (lane ^ ri);
-  }
-  const uint8_t* hsrc[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t rr = row0 + 4 * wv + 2 * h + (lane >> 5);
-    hsrc[h] = g.w + (rr < g.n ? rr : g.n - 1) * g.row_bytes + 4u * (lane & 31u);
-  }
-  const uint32_t arow = wv < static_cast<uint32_t>(B) ? wv : B - 1;
-  const uint8_t* asrc = g.aq + arow * k + 16u * lane;
-  const uint8_t* dsrc = g.ads + 8u * (arow * g.nb) + 4u * lane;
-  auto issue_weights = [&](uint32_t c, uint32_t st) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      ring_dma16_nt(wsrc[r] + 1024u * c, __builtin_amdgcn_readfirstlane(st + (4 * wv + r) * 1024u));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      ring_dma4_nt(hsrc[h] + 128u * c, __builtin_amdgcn_readfirstlane(st + kRingW + wv * 512u + h * 256u));
-  };
-  auto issue_acts = [&](uint32_t c, uint32_t st) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      ring_dma16(asrc + 2048u * c + 1024u * h,
-                 __builtin_amdgcn_readfirstlane(st + kRingW + kRingH + wv * 2048u + h * 1024u));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      ring_dma4(dsrc + 512u * c + 256u * h,
-                __builtin_amdgcn_readfirstlane(st + kRingW + kRingH + kRingA + wv * 512u + h * 256u));
-  };
+  const RingSrc src = ring_tile_src(g, row0, lane, wv);
+  const RingAct act = ring_act_src<B>(g, lane, wv);
   for (uint32_t e = threadIdx.x; e < kRingZero / 16; e += 256u)
     *reinterpret_cast<uint4*>(smem + 2 * kRingStage + 16u * e) = make_uint4(0, 0, 0, 0);
-  issue_weights(0, lds0);  // in flight while the activation is awaited
+  ring_issue_weights(src, 0, lds0, wv);  // in flight while the activation is awaited
   if constexpr (SYNC) wait_slices<B>(g, tag);
-  issue_acts(0, lds0);
+  ring_issue_acts(act, 0, lds0, wv);
 
-  // per-lane LDS read addresses
-  const uint32_t i = lane & 15u, q = lane >> 4;  // weight row (B column), k-group
-  const uint32_t aa = lane & 3u, ab = (lane & 15u) >> 2;
-  const bool anz = ab == q && aa < static_cast<uint32_t>(B);
-  // A operand: activation row aa, block 16 wv + 4 u + ab, bytes [16 h, 16 h + 16); other lanes read zeros
-  const uint32_t a_base = anz ? kRingW + kRingH + aa * 2048u + (16u * wv + ab) * 32u : 2 * kRingStage;
-  const uint32_t a_stage = anz ? kRingStage : 0u;
-  const uint32_t h_base = kRingW + (i >> 2) * 512u + (i & 3u) * 128u + 32u * wv;  // + 16 (u >> 1)
-  const uint32_t d_base = kRingW + kRingH + kRingA + (16u * wv + q) * 8u;        // + 512 a + 32 u
-  typedef int v4i __attribute__((ext_vector_type(4)));
-  v4i cinit;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) cinit[v] = kMagicBits;
-  const uint32_t msk = 0x0F0F0F0Fu;
+  const RingLane L = ring_lane<B>(lane, wv);
   float acc[B];
 #pragma unroll
   for (int a = 0; a < B; ++a) acc[a] = 0.0f;
@@ -543,38 +635,12 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
   for (uint32_t c = 0; c < nc; ++c) {
     __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));  // this wave's loads of stage c are in LDS
     __syncthreads();                               // everyone's; stage c + 1's buffer is free
-    const uint32_t cur = (c & 1u) * kRingStage;
     if (c + 1 < nc) {
       const uint32_t nxt = lds0 + ((c + 1) & 1u) * kRingStage;
-      issue_weights(c + 1, nxt);
-      issue_acts(c + 1, nxt);
+      ring_issue_weights(src, c + 1, nxt, wv);
+      ring_issue_acts(act, c + 1, nxt, wv);
     }
-    const uint8_t* ap = smem + a_base + (c & 1u) * a_stage;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t b = 16u * wv + 4u * u + q;  // this lane's block of the chunk
-      const uint4 w = *reinterpret_cast<const uint4*>(smem + cur + i * 1024u + 16u * (b ^ i));
-      const v4i a0 = *reinterpret_cast<const v4i*>(ap + 128u * u);
-      const v4i a1 = *reinterpret_cast<const v4i*>(ap + 128u * u + 16u);
-      // the unpack order of dot_nib32: low, then high nibbles of each dword
-      v4i w0, w1;
-      w0[0] = w.x & msk; w0[1] = (w.x >> 4) & msk; w0[2] = w.y & msk; w0[3] = (w.y >> 4) & msk;
-      w1[0] = w.z & msk; w1[1] = (w.z >> 4) & msk; w1[2] = w.w & msk; w1[3] = (w.w >> 4) & msk;
-      v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, w0, cinit, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, w1, d, 0, 0, 0);  // 1.5 * 2^23 + S per activation row
-      const uint4 hd = *reinterpret_cast<const uint4*>(smem + cur + h_base + 16u * (u >> 1));
-      const int j = static_cast<int>((4u * u + q) & 7u);
-      const float sw = half_bits_to_float(hd.x) * static_cast<float>(q4k_sc(hd, j));
-      const float wm = half_bits_to_float(hd.x >> 16) * static_cast<float>(q4k_mn(hd, j));
-      const float ncs = -kMagic * sw;
-#pragma unroll
-      for (int a = 0; a < B; ++a) {
-        const float2 ds = *reinterpret_cast<const float2*>(smem + cur + d_base + a * 512u + 32u * u);
-        const float t = fmaf(__int_as_float(d[a]), sw, ncs);                    // S * d * sc_j, exact
-        const float t2 = fmaf(wm, static_cast<float>(__float_as_int(ds.y)), t);  // + d_min * mn_j * A
-        acc[a] = fmaf(t2, ds.x, acc[a]);
-      }
-    }
+    ring_chunk<B>(smem, (c & 1u) * kRingStage, (c & 1u) * L.a_stage, L, acc);
   }
   // the 4 k-groups of a wave, then the 4 waves, in a fixed order
 #pragma unroll
@@ -598,6 +664,88 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
     const float v = ((part[a * 16 + r] + part[(4 + a) * 16 + r]) + part[(8 + a) * 16 + r]) + part[(12 + a) * 16 + r];
     if (row0 + r < g.n) g.y[a * g.ldy + row0 + r] = v;
   }
+}
+
+// A fixed grid walking the tiles: workgroup w takes tiles w, w + gridDim.x, ...,
+// and the ring runs on across them, so each tile's first chunk is loaded while
+// the previous tile's last one is computed. Tile j's partial sums go to LDS
+// buffer j & 1 and wave 0 stores them after the next barrier; the sums are the
+// same as the one-tile kernel's, in the same order.
+template <int B, bool SYNC>
+__global__ __launch_bounds__(256) void gemv_ring_tiles_kernel(GemvArgs g) {
+  static_assert(B >= 1 && B <= 4, "one activation row per wave");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+  const uint32_t nc = g.nb >> 6;  // the launcher guarantees nb % 64 == 0
+  const int64_t ntile = (g.n + 15) / 16;
+  const uint32_t mytiles = static_cast<uint32_t>((ntile - 1 - blockIdx.x) / gridDim.x + 1);  // grid <= tiles
+  const uint32_t total = mytiles * nc;  // stages of this workgroup
+  auto tile_row0 = [&](uint32_t j) {
+    return (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(j) * gridDim.x) * 16;
+  };
+  uint64_t tag = 0;
+  if constexpr (SYNC) {
+    tag = launch_tag();
+    produce<B>(g, tag);
+  }
+  RingSrc src = ring_tile_src(g, tile_row0(0), lane, wv);
+  const RingAct act = ring_act_src<B>(g, lane, wv);
+  for (uint32_t e = threadIdx.x; e < kRingZero / 16; e += 256u)
+    *reinterpret_cast<uint4*>(smem + 2 * kRingStage + 16u * e) = make_uint4(0, 0, 0, 0);
+  ring_issue_weights(src, 0, lds0, wv);  // in flight while the activation is awaited
+  if constexpr (SYNC) wait_slices<B>(g, tag);
+  ring_issue_acts(act, 0, lds0, wv);
+
+  const RingLane L = ring_lane<B>(lane, wv);
+  float acc[B];
+#pragma unroll
+  for (int a = 0; a < B; ++a) acc[a] = 0.0f;
+  float* part = reinterpret_cast<float*>(smem + 2 * kRingStage + kRingZero);  // [2][4 waves][4][16]
+  auto store_tile = [&](uint32_t j) {
+    if (wv == 0 && lane < 16u * B) {
+      const float* pp = part + (j & 1u) * 256u;
+      const uint32_t a = lane >> 4, r = lane & 15u;
+      const float v = ((pp[a * 16 + r] + pp[(4 + a) * 16 + r]) + pp[(8 + a) * 16 + r]) + pp[(12 + a) * 16 + r];
+      const int64_t row = tile_row0(j) + r;
+      if (row < g.n) g.y[a * g.ldy + row] = v;
+    }
+  };
+
+  uint32_t j = 0, c = 0;  // tile and chunk of stage s
+  for (uint32_t s = 0; s < total; ++s) {
+    __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));  // this wave's loads of stage s are in LDS
+    __syncthreads();                               // everyone's; stage s + 1's buffer is free
+    if (c == 0 && j > 0) store_tile(j - 1);
+    if (s + 1 < total) {
+      const uint32_t nxt = lds0 + ((s + 1) & 1u) * kRingStage;
+      uint32_t cn = c + 1;
+      if (cn == nc) {
+        cn = 0;
+        src = ring_tile_src(g, tile_row0(j + 1), lane, wv);
+      }
+      ring_issue_weights(src, cn, nxt, wv);
+      ring_issue_acts(act, cn, nxt, wv);
+    }
+    ring_chunk<B>(smem, (s & 1u) * kRingStage, (s & 1u) * L.a_stage, L, acc);
+    if (++c == nc) {
+      // the 4 k-groups of a wave, then (in store_tile) the 4 waves, in a fixed order
+#pragma unroll
+      for (int a = 0; a < B; ++a) {
+        float v = acc[a];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (lane < 16) part[(j & 1u) * 256u + (wv * 4 + a) * 16 + lane] = v;
+        acc[a] = 0.0f;
+      }
+      c = 0;
+      ++j;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));
+  __syncthreads();
+  store_tile(j - 1);
 }
 
 // Several independent products in one launch (a descriptor list, e.g. the
@@ -825,11 +973,15 @@ hipError_t launch_cfg(const Plan& p, hipStream_t s) {
 // The matrix-core kernel: one 16-row tile per workgroup (Q4_K, 3-4 rows,
 // k a multiple of 2048; select_gemv only picks it there).
 template <int TYPE, int B, bool SYNC>
-hipError_t launch_ring(const Plan& p, hipStream_t s) {
+hipError_t launch_ring(const Plan& p, bool tiles_grid, hipStream_t s) {
   if constexpr (TYPE == kQ4_K && B >= 3 && B <= 4) {
     if (p.nb % 64 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemv_ring_kernel<B, SYNC>), dim3(static_cast<uint32_t>((p.n + 15) / 16)), dim3(256),
-                       kRingLds, s, make_args(p));
+    if (tiles_grid)
+      hipLaunchKernelGGL((gemv_ring_tiles_kernel<B, SYNC>), dim3(static_cast<uint32_t>(kRingGrid)), dim3(256),
+                         kRingTilesLds, s, make_args(p));
+    else
+      hipLaunchKernelGGL((gemv_ring_kernel<B, SYNC>), dim3(static_cast<uint32_t>((p.n + 15) / 16)), dim3(256),
+                         kRingLds, s, make_args(p));
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
@@ -856,7 +1008,7 @@ hipError_t launch_b(const Plan& p, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   } else {
-    if (v.ring) return launch_ring<TYPE, B, SYNC>(p, s);
+    if (v.ring) return launch_ring<TYPE, B, SYNC>(p, v.ring_tiles, s);
     if (v.waves == 8) {
       if (ru == 81) return launch_cfg<TYPE, B, 8, 1, SYNC, 8>(p, s);
       if (ru == 41) return launch_cfg<TYPE, B, 4, 1, SYNC, 8>(p, s);

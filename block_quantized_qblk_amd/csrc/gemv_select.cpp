@@ -31,8 +31,15 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
   // faster on every 70B- and 7B-shaped matrix (70B layer 103 against 118 us;
   // down 25.6 against 33.7 us), at 3 rows on all but the 7B q/k/v (6.07
   // against 6.06 us); at 2 rows faster on only 2 of 8, so not used there.
+  // With more 16-row tiles than the two-per-CU grid holds, a fixed grid walks
+  // them (gemv_ring_tiles_kernel), so that each tile's first chunk loads while
+  // the last one's is computed: 70B gate/up with the in-launch quantization
+  // 50-52 against 56 us at 4 rows, 48 against 55 at 3, q/k/v (640 tiles) 14.9
+  // against 15.4 us; at 512 tiles or fewer (70B o and down) the one-tile
+  // kernel stays faster (o 10.9 against 11.3 us).
   if (type == kQ4_K && (b == 3 || b == 4) && k % 2048 == 0) {
     v.ring = true;
+    v.ring_tiles = (n + 15) / 16 > kRingGrid;
     return v;
   }
   if (mode == kGemvLdsFused) {
@@ -91,7 +98,7 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len) {
   const char* t = v.sync ? "true" : "false";
   const char* a = v.alds ? "true" : "false";
-  if (v.ring) return snprintf(buf, len, "gemv_ring_kernel<%d, %s>", v.b, t);
+  if (v.ring) return snprintf(buf, len, "%s<%d, %s>", v.ring_tiles ? "gemv_ring_tiles_kernel" : "gemv_ring_kernel", v.b, t);
   if (v.pipe)
     return snprintf(buf, len, "gemv_pipe_kernel<%d, %d, %d, %s, %s, %s>", v.type, v.b, v.r,
                     v.fused ? "true" : "false", t, a);

@@ -96,8 +96,9 @@ constexpr bool gemv_stage_acts_in_lds(int b, int64_t nb) {
 }
 // Which GEMV kernel instance a product runs (pure host logic, no GPU):
 // gemv_kernel<type, b, r, u, sync, alds, waves>, gemv_pipe_kernel<type,
-// b, r, fused, sync, alds> or gemv_ring_kernel<b, sync>. mode: how the
-// activation reaches the kernel.
+// b, r, fused, sync, alds>, gemv_ring_kernel<b, sync> or
+// gemv_ring_tiles_kernel<b, sync>. mode: how the activation reaches the
+// kernel.
 enum : int { kGemvQuantized = 0, kGemvLdsFused = 1, kGemvInLaunch = 2 };
 struct GemvVariant {
   int type;
@@ -110,7 +111,11 @@ struct GemvVariant {
   bool fused; // activation quantized in every workgroup's LDS
   int waves;  // waves per workgroup (classic kernel)
   bool ring;  // gemv_ring_kernel (Q4_K, 3-4 rows: matrix cores, direct-load LDS ring)
+  bool ring_tiles;  // ... as gemv_ring_tiles_kernel, a fixed grid walking the 16-row tiles
 };
+// The tile-walking grid of the matrix-core GEMV (two workgroups per CU); used
+// when the 16-row tiles outnumber it.
+constexpr int64_t kRingGrid = 512;
 GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode);
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len);
 // Where the in-launch handoff keeps its data: the activation buffer

@@ -16,7 +16,10 @@ GEMV_RANDOM = [(37, 1024, 1), (300, 4096, 1), (129, 2304, 4), (64, 256, 8), (70,
                (1000, 2048, 3), (5, 4096, 4)]
 
 # Q4_K's matrix-core kernel with exact fp32 arithmetic: (n, k, batch)
-GEMV_RING_EXACT = [(67, 4096, 3), (67, 4096, 4), (16, 2048, 4)]
+GEMV_RING_EXACT = [(67, 4096, 3), (67, 4096, 4), (16, 2048, 4),
+                   # more than 512 tiles (the tile-walking grid): a ragged last tile, and
+                   # 1025 tiles, so that one workgroup takes three and the others two
+                   (8200, 2048, 3), (16400, 2048, 4)]
 
 # qblk_gemv with exact fp32 arithmetic, every type: batch (n = 67, k = 2304 / 2336)
 GEMV_EXACT_BATCH = [1, 3, 8, 11]

@@ -235,7 +235,9 @@ def test_gemv_variant_names():
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 1, True) == \
         "gemv_kernel<3, 1, 4, 1, true, true, 4>"
     # Q4_K at 3-4 activation rows with k a multiple of 2048: the matrix-core kernel
-    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 4, True) == "gemv_ring_kernel<4, true>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 4, True) == "gemv_ring_tiles_kernel<4, true>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8208, 2048, 3, False) == "gemv_ring_tiles_kernel<3, false>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 2048, 3, False) == "gemv_ring_kernel<3, false>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 8192, 3, False) == "gemv_ring_kernel<3, false>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 2304, 4, True) == "gemv_kernel<3, 4, 2, 1, true, true, 4>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 8, True) == "gemv_kernel<3, 8, 8, 1, true, false, 4>"

@@ -198,7 +198,7 @@ def test_gemv_ring_exact_arithmetic(n, k, batch):
     with power-of-two scales: every partial sum is exact in fp32, so y must
     equal the oracle bit for bit whatever the summation order."""
     print(f"gemv ring exact n={n} k={k} batch={batch}", flush=True)
-    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, n, k, batch, False).startswith("gemv_ring_kernel")
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, n, k, batch, False).startswith("gemv_ring")
     packed, x, y32 = _exact_case(o.TYPE_Q4_K, n, k, batch, 950 + batch)
     y = qblk.qblk_gemv(o.TYPE_Q4_K, dev(packed.reshape(-1)), n, k, dev_quantize(x), batch)
     assert np.array_equal(host(y), y32)
@@ -643,7 +643,7 @@ def test_gemv_multi_matches_single_products(wtype, batch, ks):
     qblk.qblk_gemv_multi(wtype, prods, batch)
     for (w, x, ysingle, ybig), (_, n, k, _, _) in zip(refs, prods):
         yh = host(ybig)
-        if qblk.qblk_gemv_variant(wtype, n, k, batch, False).startswith("gemv_ring_kernel"):
+        if qblk.qblk_gemv_variant(wtype, n, k, batch, False).startswith("gemv_ring"):
             # qblk_gemv runs the matrix-core kernel here: the same block
             # products and scale steps, summed in another order
             ys = host(ysingle)
