@@ -397,8 +397,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   gemv_body<TYPE, B, R, U, SYNC, ALDS, WAVES>(g, blockIdx.x);
 }
 
-// ---------------------------------------------------------------- matrix-core form, 3-4 activation rows
-// Q4_K with 3 or 4 activation rows and k a multiple of 2048. The dot4 form
+// ---------------------------------------------------------------- matrix-core form, 2-4 activation rows
+// Q4_K with 2 to 4 activation rows and k a multiple of 2048. The dot4 form
 // spends 73 VALU instructions per row and block at 4 rows (32 of them
 // dot4); here each block's integer dots run on v_mfma_i32_16x16x64_i8 and
 // the VALU keeps the unpack, the scale decode and the scale FMAs (about 40).
@@ -970,11 +970,11 @@ hipError_t launch_cfg(const Plan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The matrix-core kernel: one 16-row tile per workgroup (Q4_K, 3-4 rows,
+// The matrix-core kernel: one 16-row tile per workgroup (Q4_K, 2-4 rows,
 // k a multiple of 2048; select_gemv only picks it there).
 template <int TYPE, int B, bool SYNC>
 hipError_t launch_ring(const Plan& p, bool tiles_grid, hipStream_t s) {
-  if constexpr (TYPE == kQ4_K && B >= 3 && B <= 4) {
+  if constexpr (TYPE == kQ4_K && B >= 2 && B <= 4) {
     if (p.nb % 64 != 0) return hipErrorInvalidValue;
     if (tiles_grid)
       hipLaunchKernelGGL((gemv_ring_tiles_kernel<B, SYNC>), dim3(static_cast<uint32_t>(kRingGrid)), dim3(256),

@@ -25,19 +25,13 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
   v.sync = mode == kGemvInLaunch;
   v.fused = mode == kGemvLdsFused;
   const int64_t nb = k / 32;
-  // Q4_K at 3-4 activation rows with whole 2048-element chunks: the
+  // Q4_K at 2-4 activation rows with whole 2048-element chunks: the
   // matrix-core kernel with the direct-load LDS ring (gemv_ring_kernel).
-  // Measured against the dot4 kernels on a quantized activation: at 4 rows
-  // faster on every 70B- and 7B-shaped matrix (70B layer 103 against 118 us;
-  // down 25.6 against 33.7 us), at 3 rows on all but the 7B q/k/v (6.07
-  // against 6.06 us); at 2 rows faster on only 2 of 8, so not used there.
-  // With more 16-row tiles than the two-per-CU grid holds, a fixed grid walks
-  // them (gemv_ring_tiles_kernel), so that each tile's first chunk loads while
-  // the last one's is computed: 70B gate/up with the in-launch quantization
-  // 50-52 against 56 us at 4 rows, 48 against 55 at 3, q/k/v (640 tiles) 14.9
-  // against 15.4 us; at 512 tiles or fewer (70B o and down) the one-tile
-  // kernel stays faster (o 10.9 against 11.3 us).
-  if (type == kQ4_K && (b == 3 || b == 4) && k % 2048 == 0) {
+  // Measured against the dot4 kernels with the in-launch quantization, it is
+  // faster on every 70B-, 7B- and shard-shaped matrix at 2, 3 and 4 rows
+  // (at 2 rows: 70B gate/up 44.7-47.1 against 49.5-49.9 us, down 24.9
+  // against 27.2, o 10.5 against 11.7, 7B down 11.4 against 16.0).
+  if (type == kQ4_K && b >= 2 && b <= 4 && k % 2048 == 0) {
     v.ring = true;
     v.ring_tiles = (n + 15) / 16 > kRingGrid;
     return v;

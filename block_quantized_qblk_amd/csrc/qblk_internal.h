@@ -110,7 +110,7 @@ struct GemvVariant {
   bool alds;  // activation rows staged in LDS
   bool fused; // activation quantized in every workgroup's LDS
   int waves;  // waves per workgroup (classic kernel)
-  bool ring;  // gemv_ring_kernel (Q4_K, 3-4 rows: matrix cores, direct-load LDS ring)
+  bool ring;  // gemv_ring_kernel (Q4_K, 2-4 rows: matrix cores, direct-load LDS ring)
   bool ring_tiles;  // ... as gemv_ring_tiles_kernel, a fixed grid walking the 16-row tiles
 };
 // The tile-walking grid of the matrix-core GEMV (two workgroups per CU); used

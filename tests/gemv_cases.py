@@ -11,12 +11,12 @@ GEMV_RANDOM = [(37, 1024, 1), (300, 4096, 1), (129, 2304, 4), (64, 256, 8), (70,
                (3100, 512, 2), (16400, 512, 5),
                # a single row and two rows: one wave, most lanes past the last row
                (1, 256, 1), (2, 512, 3),
-               # Q4_K's matrix-core kernel (3-4 rows, k a multiple of 2048): one
+               # Q4_K's matrix-core kernel (2-4 rows, k a multiple of 2048): one
                # 2048-element chunk with a ragged last tile, and fewer rows than a tile
                (1000, 2048, 3), (5, 4096, 4)]
 
 # Q4_K's matrix-core kernel with exact fp32 arithmetic: (n, k, batch)
-GEMV_RING_EXACT = [(67, 4096, 3), (67, 4096, 4), (16, 2048, 4),
+GEMV_RING_EXACT = [(67, 4096, 2), (67, 4096, 3), (67, 4096, 4), (16, 2048, 4), (8208, 2048, 2),
                    # more than 512 tiles (the tile-walking grid): a ragged last tile, and
                    # 1025 tiles, so that one workgroup takes three and the others two
                    (8200, 2048, 3), (16400, 2048, 4)]
