@@ -397,8 +397,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
   gemv_body<TYPE, B, R, U, SYNC, ALDS, WAVES>(g, blockIdx.x);
 }
 
-// ---------------------------------------------------------------- matrix-core form, 2-4 activation rows
-// Q4_K with 2 to 4 activation rows and k a multiple of 2048. The dot4 form
+// ---------------------------------------------------------------- matrix-core form, 2-8 activation rows
+// Q4_K with 2 to 8 activation rows and k a multiple of 2048. The dot4 form
 // spends 73 VALU instructions per row and block at 4 rows (32 of them
 // dot4); here each block's integer dots run on v_mfma_i32_16x16x64_i8 and
 // the VALU keeps the unpack, the scale decode and the scale FMAs (about 40).
@@ -406,11 +406,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
 // Operands (D = A x B, 16 x 16, K = 64): B holds 16 weight rows (column i =
 // lane & 15), its k-group q = lane >> 4 holds half of block 4u + q of the
 // step (two MFMAs per block pair of halves). A row m = 4 b + a (activation
-// row a, block b of the step) is nonzero only in k-group b, so output
-// D[4 q + a][i] is the integer dot of weight row i with activation row a
-// over one whole block: lane (i, q) ends with the four activation rows of its
-// own row and block, whose scales it decoded itself. A quarter of the MFMA
-// work is useful; the matrix cores have that to spare.
+// row a of a group of four, block b of the step) is nonzero only in k-group
+// b, so output D[4 q + a][i] is the integer dot of weight row i with
+// activation row a over one whole block: lane (i, q) ends with the four
+// activation rows of its own row and block, whose scales it decoded itself
+// (5-8 rows: a second group, two more MFMAs on the same B operand). A
+// quarter of the MFMA work is useful; the matrix cores have that to spare.
 //
 // Data movement: that operand layout needs 16 rows per load, and 16-row
 // loads of 64 bytes each stream at about two thirds of the bandwidth of the
@@ -433,13 +434,26 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs g) {
 // ring. Nothing else in the loop touches vector memory.
 constexpr uint32_t kRingW = 16384;   // 16 rows x 1 KiB of codes
 constexpr uint32_t kRingH = 2048;    // 16 rows x 128 B of headers
-constexpr uint32_t kRingA = 8192;    // 4 activation rows x 2 KiB of codes
-constexpr uint32_t kRingD = 2048;    // 4 activation rows x 64 (d, sum) pairs
-constexpr uint32_t kRingStage = kRingW + kRingH + kRingA + kRingD;
 constexpr uint32_t kRingZero = 512;  // zero operand slots of the unused A lanes
-constexpr uint32_t kRingLds = 2 * kRingStage + kRingZero;
-constexpr uint32_t kRingTilesLds = kRingLds + 2048;  // + the partial sums of two tiles, [2][4][4][16]
-constexpr int kRingDma = 10;         // direct loads per wave and stage
+// A stage holds the weights, the headers, then NA activation slots (4 for up
+// to 4 rows, 8 for 5-8; slot a holds activation row min(a, rows - 1)): NA x
+// 2 KiB of codes, then NA x 64 (d, sum) pairs. Two stages, then the zero
+// slots; the tile-walking kernel adds one tile's partial sums, [4 waves][NA][16].
+template <int NA>
+struct RingLayout {
+  static constexpr uint32_t kA = kRingW + kRingH;
+  static constexpr uint32_t kD = kA + NA * 2048u;
+  static constexpr uint32_t kStage = kD + NA * 512u;
+  static constexpr uint32_t kZero = 2 * kStage;
+  static constexpr uint32_t kLds = kZero + kRingZero;
+  static constexpr uint32_t kPart = kLds;
+  static constexpr uint32_t kTilesLds = kPart + 4u * NA * 16u * 4u;
+  static_assert(2 * kTilesLds <= 160u * 1024u, "two workgroups per CU");
+};
+template <int B>
+constexpr int ring_slots() {
+  return B > 4 ? 8 : 4;
+}
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -506,60 +520,78 @@ __device__ __forceinline__ void ring_issue_weights(const RingSrc& src, uint32_t 
   for (int h = 0; h < 2; ++h)
     ring_dma4_nt(src.h[h] + 128u * c, __builtin_amdgcn_readfirstlane(st + kRingW + wv * 512u + h * 256u));
 }
-// chunk c of activation row min(wv, B - 1): its codes, 16-B unit U fetched into
-// unit U ^ ((wv & 1) | (wv & 2) << 2) of slot wv, and its (d, sum) pairs
+// Activation slots 4 t + wv of this wave (t < NA / 4), row min(slot, B - 1):
+// codes with 16-B unit U fetched into unit U ^ ((wv & 1) | (wv & 2) << 2) of
+// the slot, and (d, sum) pairs.
+template <int B>
 struct RingAct {
-  const uint8_t* a;
-  const uint8_t* d;
+  const uint8_t* a[ring_slots<B>() / 4];
+  const uint8_t* d[ring_slots<B>() / 4];
 };
 template <int B>
-__device__ __forceinline__ RingAct ring_act_src(const GemvArgs& g, uint32_t lane, uint32_t wv) {
-  const uint32_t arow = wv < static_cast<uint32_t>(B) ? wv : B - 1;
+__device__ __forceinline__ RingAct<B> ring_act_src(const GemvArgs& g, uint32_t lane, uint32_t wv) {
+  RingAct<B> src;
   const uint32_t asw = (wv & 1u) | ((wv & 2u) << 2);
-  return RingAct{g.aq + arow * g.nb * 32u + 16u * (lane ^ asw), g.ads + 8u * (arow * g.nb) + 4u * lane};
+#pragma unroll
+  for (int t = 0; t < ring_slots<B>() / 4; ++t) {
+    const uint32_t slot = 4u * t + wv;
+    const uint32_t arow = slot < static_cast<uint32_t>(B) ? slot : B - 1;
+    src.a[t] = g.aq + arow * g.nb * 32u + 16u * (lane ^ asw);
+    src.d[t] = g.ads + 8u * (arow * g.nb) + 4u * lane;
+  }
+  return src;
 }
-__device__ __forceinline__ void ring_issue_acts(const RingAct& src, uint32_t c, uint32_t st, uint32_t wv) {
+template <int B>
+__device__ __forceinline__ void ring_issue_acts(const RingAct<B>& src, uint32_t c, uint32_t st, uint32_t wv) {
+  typedef RingLayout<ring_slots<B>()> L;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-    ring_dma16(src.a + 2048u * c + 1024u * h,
-               __builtin_amdgcn_readfirstlane(st + kRingW + kRingH + wv * 2048u + h * 1024u));
+  for (int t = 0; t < ring_slots<B>() / 4; ++t) {
+    const uint32_t slot = 4u * t + wv;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-    ring_dma4(src.d + 512u * c + 256u * h,
-              __builtin_amdgcn_readfirstlane(st + kRingW + kRingH + kRingA + wv * 512u + h * 256u));
+    for (int h = 0; h < 2; ++h)
+      ring_dma16(src.a[t] + 2048u * c + 1024u * h, __builtin_amdgcn_readfirstlane(st + L::kA + slot * 2048u + h * 1024u));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ring_dma4(src.d[t] + 512u * c + 256u * h, __builtin_amdgcn_readfirstlane(st + L::kD + slot * 512u + h * 256u));
+  }
 }
 
 // Per-lane LDS read addresses of a stage (relative to the stage).
+template <int NG>  // groups of 4 activation rows
 struct RingLane {
-  uint32_t w_row;       // weight row i's KiB
-  uint32_t w_blk;       // 16 wv + q: the lane's block at u = 0 (+ 4 u), XORed with i
+  uint32_t w_row;             // weight row i's KiB
+  uint32_t w_blk;             // 16 wv + q: the lane's block at u = 0 (+ 4 u), XORed with i
   uint32_t i;
-  uint32_t a_base[2][2];  // A operand [u & 1][half] (+ 256 (u >> 1)); zero lanes: the zero slots
-  uint32_t a_stage;       // stage stride of the A reads (0 for the zero lanes)
-  uint32_t h_base[2];     // row i's header of super-block 2 wv + (u >> 1)
-  uint32_t d_base;        // (d, sum) of block 16 wv + q of activation row 0 (+ 512 a + 32 u)
+  uint32_t a_base[NG][2][2];  // A operand of group G [u & 1][half] (+ 256 (u >> 1)); zero lanes: the zero slots
+  uint32_t a_stage[NG];       // stage stride of the A reads (0 for the zero lanes)
+  uint32_t h_base[2];         // row i's header of super-block 2 wv + (u >> 1)
+  uint32_t d_base;            // (d, sum) of block 16 wv + q of activation row 0 (+ 512 a + 32 u)
   uint32_t q;
 };
 template <int B>
-__device__ __forceinline__ RingLane ring_lane(uint32_t lane, uint32_t wv) {
-  RingLane L;
+__device__ __forceinline__ RingLane<ring_slots<B>() / 4> ring_lane(uint32_t lane, uint32_t wv) {
+  typedef RingLayout<ring_slots<B>()> Lay;
+  RingLane<ring_slots<B>() / 4> L;
   const uint32_t i = lane & 15u, q = lane >> 4;  // weight row (B column), k-group
   const uint32_t aa = lane & 3u, ab = (lane & 15u) >> 2;
-  // A operand: activation row aa, block 16 wv + 4 u + ab, bytes [16 h, 16 h + 16), unit
-  // 32 wv + 8 u + 2 q + h swizzled as the loads placed it; the lanes outside row ab == q
-  // of their k-group read zeros, from a slot that the active lanes of that k-group leave free
-  const bool anz = ab == q && aa < static_cast<uint32_t>(B);
+  // A operand of group G: activation row 4 G + aa, block 16 wv + 4 u + ab, bytes [16 h, 16 h + 16),
+  // unit 32 wv + 8 u + 2 q + h swizzled as the loads placed it; the lanes outside row ab == q of
+  // their k-group read zeros, from a slot that the active lanes of that k-group leave free
 #pragma unroll
-  for (int uo = 0; uo < 2; ++uo)
+  for (int G = 0; G < ring_slots<B>() / 4; ++G) {
+    const bool anz = ab == q && 4u * G + aa < static_cast<uint32_t>(B);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      L.a_base[uo][hh] = anz ? kRingW + kRingH + aa * 2048u +
-                                   16u * (32u * wv + 8u * (uo ^ (aa >> 1)) + 2u * q + (hh ^ (aa & 1u)))
-                             : 2 * kRingStage + 16u * (2u * q + 4u);
-  L.a_stage = anz ? kRingStage : 0u;
+    for (int uo = 0; uo < 2; ++uo)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        L.a_base[G][uo][hh] = anz ? Lay::kA + (4u * G + aa) * 2048u +
+                                        16u * (32u * wv + 8u * (uo ^ (aa >> 1)) + 2u * q + (hh ^ (aa & 1u)))
+                                  : Lay::kZero + 16u * (2u * q + 4u);
+    L.a_stage[G] = anz ? Lay::kStage : 0u;
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t) L.h_base[t] = kRingW + 128u * i + 16u * ((2u * wv + t) ^ ((i >> 1) & 7u));
-  L.d_base = kRingW + kRingH + kRingA + (16u * wv + q) * 8u;
+  L.d_base = Lay::kD + (16u * wv + q) * 8u;
   L.w_row = i * 1024u;
   L.w_blk = 16u * wv + q;
   L.i = i;
@@ -567,11 +599,13 @@ __device__ __forceinline__ RingLane ring_lane(uint32_t lane, uint32_t wv) {
   return L;
 }
 
-// The stage at LDS offset cur (A reads at + ast): 4 steps of 2 MFMAs, each
-// followed by this lane's scale steps for its (row, block).
+// The stage of parity par: 4 steps of 2 MFMAs per group of 4 activation
+// rows, each followed by this lane's scale steps for its (row, block).
 template <int B>
-__device__ __forceinline__ void ring_chunk(const uint8_t* smem, uint32_t cur, uint32_t ast, const RingLane& L,
+__device__ __forceinline__ void ring_chunk(const uint8_t* smem, uint32_t par, const RingLane<ring_slots<B>() / 4>& L,
                                            float (&acc)[B]) {
+  constexpr int NG = ring_slots<B>() / 4;
+  const uint32_t cur = par * RingLayout<ring_slots<B>()>::kStage;
   typedef int v4i __attribute__((ext_vector_type(4)));
   v4i cinit;
 #pragma unroll
@@ -581,14 +615,19 @@ __device__ __forceinline__ void ring_chunk(const uint8_t* smem, uint32_t cur, ui
   for (int u = 0; u < 4; ++u) {
     const uint32_t b = L.w_blk + 4u * u;  // this lane's block of the chunk
     const uint4 w = *reinterpret_cast<const uint4*>(smem + cur + L.w_row + 16u * (b ^ L.i));
-    const v4i a0 = *reinterpret_cast<const v4i*>(smem + L.a_base[u & 1][0] + ast + 256u * (u >> 1));
-    const v4i a1 = *reinterpret_cast<const v4i*>(smem + L.a_base[u & 1][1] + ast + 256u * (u >> 1));
     // the unpack order of dot_nib32: low, then high nibbles of each dword
     v4i w0, w1;
     w0[0] = w.x & msk; w0[1] = (w.x >> 4) & msk; w0[2] = w.y & msk; w0[3] = (w.y >> 4) & msk;
     w1[0] = w.z & msk; w1[1] = (w.z >> 4) & msk; w1[2] = w.w & msk; w1[3] = (w.w >> 4) & msk;
-    v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, w0, cinit, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, w1, d, 0, 0, 0);  // 1.5 * 2^23 + S per activation row
+    v4i d[NG];
+#pragma unroll
+    for (int G = 0; G < NG; ++G) {
+      const uint32_t ao = par * L.a_stage[G] + 256u * (u >> 1);
+      const v4i a0 = *reinterpret_cast<const v4i*>(smem + L.a_base[G][u & 1][0] + ao);
+      const v4i a1 = *reinterpret_cast<const v4i*>(smem + L.a_base[G][u & 1][1] + ao);
+      d[G] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, w0, cinit, 0, 0, 0);
+      d[G] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, w1, d[G], 0, 0, 0);  // 1.5 * 2^23 + S per activation row
+    }
     const uint4 hd = *reinterpret_cast<const uint4*>(smem + cur + L.h_base[u >> 1]);
     const int j = static_cast<int>((4u * u + L.q) & 7u);
     const float sw = half_bits_to_float(hd.x) * static_cast<float>(q4k_sc(hd, j));
@@ -597,17 +636,32 @@ __device__ __forceinline__ void ring_chunk(const uint8_t* smem, uint32_t cur, ui
 #pragma unroll
     for (int a = 0; a < B; ++a) {
       const float2 ds = *reinterpret_cast<const float2*>(smem + cur + L.d_base + a * 512u + 32u * u);
-      const float t = fmaf(__int_as_float(d[a]), sw, ncs);                    // S * d * sc_j, exact
+      const float t = fmaf(__int_as_float(d[a >> 2][a & 3]), sw, ncs);          // S * d * sc_j, exact
       const float t2 = fmaf(wm, static_cast<float>(__float_as_int(ds.y)), t);  // + d_min * mn_j * A
       acc[a] = fmaf(t2, ds.x, acc[a]);
     }
   }
 }
 
+// Wave w < ceil(B / 4) adds the 4 waves' partial sums of activation rows 4 w ..
+// 4 w + 3, in wave order, and stores them (rows from row0 on).
+template <int B>
+__device__ __forceinline__ void ring_store(const GemvArgs& g, const float* part, int64_t row0, uint32_t lane,
+                                           uint32_t wv) {
+  constexpr uint32_t NA = ring_slots<B>();
+  const uint32_t a = 4u * wv + (lane >> 4), r = lane & 15u;
+  if (a < static_cast<uint32_t>(B)) {
+    const float v = ((part[a * 16 + r] + part[(NA + a) * 16 + r]) + part[(2 * NA + a) * 16 + r]) +
+                    part[(3 * NA + a) * 16 + r];
+    if (row0 + r < g.n) g.y[a * g.ldy + row0 + r] = v;
+  }
+}
+
 // One 16-row tile per workgroup (grid = tiles).
 template <int B, bool SYNC>
 __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
-  static_assert(B >= 1 && B <= 4, "one activation row per wave");
+  static_assert(B >= 1 && B <= 8, "up to 8 activation rows");
+  typedef RingLayout<ring_slots<B>()> Lay;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -620,14 +674,14 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
     produce<B>(g, tag);
   }
   const RingSrc src = ring_tile_src(g, row0, lane, wv);
-  const RingAct act = ring_act_src<B>(g, lane, wv);
+  const RingAct<B> act = ring_act_src<B>(g, lane, wv);
   for (uint32_t e = threadIdx.x; e < kRingZero / 16; e += 256u)
-    *reinterpret_cast<uint4*>(smem + 2 * kRingStage + 16u * e) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(smem + Lay::kZero + 16u * e) = make_uint4(0, 0, 0, 0);
   ring_issue_weights(src, 0, lds0, wv);  // in flight while the activation is awaited
   if constexpr (SYNC) wait_slices<B>(g, tag);
-  ring_issue_acts(act, 0, lds0, wv);
+  ring_issue_acts<B>(act, 0, lds0, wv);
 
-  const RingLane L = ring_lane<B>(lane, wv);
+  const auto L = ring_lane<B>(lane, wv);
   float acc[B];
 #pragma unroll
   for (int a = 0; a < B; ++a) acc[a] = 0.0f;
@@ -636,11 +690,11 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
     __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));  // this wave's loads of stage c are in LDS
     __syncthreads();                               // everyone's; stage c + 1's buffer is free
     if (c + 1 < nc) {
-      const uint32_t nxt = lds0 + ((c + 1) & 1u) * kRingStage;
+      const uint32_t nxt = lds0 + ((c + 1) & 1u) * Lay::kStage;
       ring_issue_weights(src, c + 1, nxt, wv);
-      ring_issue_acts(act, c + 1, nxt, wv);
+      ring_issue_acts<B>(act, c + 1, nxt, wv);
     }
-    ring_chunk<B>(smem, (c & 1u) * kRingStage, (c & 1u) * L.a_stage, L, acc);
+    ring_chunk<B>(smem, c & 1u, L, acc);
   }
   // the 4 k-groups of a wave, then the 4 waves, in a fixed order
 #pragma unroll
@@ -652,33 +706,32 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));
   __syncthreads();  // every wave is done with the stages
-  float* part = reinterpret_cast<float*>(smem);  // [4 waves][4][16]
+  float* part = reinterpret_cast<float*>(smem);  // [4 waves][NA][16]
   if (lane < 16) {
 #pragma unroll
-    for (int a = 0; a < B; ++a) part[(wv * 4 + a) * 16 + lane] = acc[a];
+    for (int a = 0; a < B; ++a) part[(wv * ring_slots<B>() + a) * 16 + lane] = acc[a];
   }
   __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));
   __syncthreads();
-  if (wv == 0 && lane < 16u * B) {
-    const uint32_t a = lane >> 4, r = lane & 15u;
-    const float v = ((part[a * 16 + r] + part[(4 + a) * 16 + r]) + part[(8 + a) * 16 + r]) + part[(12 + a) * 16 + r];
-    if (row0 + r < g.n) g.y[a * g.ldy + row0 + r] = v;
-  }
+  ring_store<B>(g, part, row0, lane, wv);
 }
 
 // A fixed grid walking the tiles: workgroup w takes tiles w, w + gridDim.x, ...,
 // and the ring runs on across them, so each tile's first chunk is loaded while
-// the previous tile's last one is computed. Tile j's partial sums go to LDS
-// buffer j & 1 and wave 0 stores them after the next barrier; the sums are the
-// same as the one-tile kernel's, in the same order.
+// the previous tile's last one is computed. The waves' partial sums of tile j
+// go to LDS at the end of its last chunk, and are added and stored after the
+// next barrier; a tile has at least two chunks (the launcher), so the next
+// tile's sums are written after one more barrier, when those reads are done.
+// The sums are the one-tile kernel's, in the same order.
 template <int B, bool SYNC>
 __global__ __launch_bounds__(256) void gemv_ring_tiles_kernel(GemvArgs g) {
-  static_assert(B >= 1 && B <= 4, "one activation row per wave");
+  static_assert(B >= 1 && B <= 8, "up to 8 activation rows");
+  typedef RingLayout<ring_slots<B>()> Lay;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-  const uint32_t nc = g.nb >> 6;  // the launcher guarantees nb % 64 == 0
+  const uint32_t nc = g.nb >> 6;  // the launcher guarantees nb % 64 == 0 and nc >= 2
   const int64_t ntile = (g.n + 15) / 16;
   const uint32_t mytiles = static_cast<uint32_t>((ntile - 1 - blockIdx.x) / gridDim.x + 1);  // grid <= tiles
   const uint32_t total = mytiles * nc;  // stages of this workgroup
@@ -691,52 +744,43 @@ __global__ __launch_bounds__(256) void gemv_ring_tiles_kernel(GemvArgs g) {
     produce<B>(g, tag);
   }
   RingSrc src = ring_tile_src(g, tile_row0(0), lane, wv);
-  const RingAct act = ring_act_src<B>(g, lane, wv);
+  const RingAct<B> act = ring_act_src<B>(g, lane, wv);
   for (uint32_t e = threadIdx.x; e < kRingZero / 16; e += 256u)
-    *reinterpret_cast<uint4*>(smem + 2 * kRingStage + 16u * e) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(smem + Lay::kZero + 16u * e) = make_uint4(0, 0, 0, 0);
   ring_issue_weights(src, 0, lds0, wv);  // in flight while the activation is awaited
   if constexpr (SYNC) wait_slices<B>(g, tag);
-  ring_issue_acts(act, 0, lds0, wv);
+  ring_issue_acts<B>(act, 0, lds0, wv);
 
-  const RingLane L = ring_lane<B>(lane, wv);
+  const auto L = ring_lane<B>(lane, wv);
   float acc[B];
 #pragma unroll
   for (int a = 0; a < B; ++a) acc[a] = 0.0f;
-  float* part = reinterpret_cast<float*>(smem + 2 * kRingStage + kRingZero);  // [2][4 waves][4][16]
-  auto store_tile = [&](uint32_t j) {
-    if (wv == 0 && lane < 16u * B) {
-      const float* pp = part + (j & 1u) * 256u;
-      const uint32_t a = lane >> 4, r = lane & 15u;
-      const float v = ((pp[a * 16 + r] + pp[(4 + a) * 16 + r]) + pp[(8 + a) * 16 + r]) + pp[(12 + a) * 16 + r];
-      const int64_t row = tile_row0(j) + r;
-      if (row < g.n) g.y[a * g.ldy + row] = v;
-    }
-  };
+  float* part = reinterpret_cast<float*>(smem + Lay::kPart);  // [4 waves][NA][16]
 
   uint32_t j = 0, c = 0;  // tile and chunk of stage s
   for (uint32_t s = 0; s < total; ++s) {
     __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));  // this wave's loads of stage s are in LDS
     __syncthreads();                               // everyone's; stage s + 1's buffer is free
-    if (c == 0 && j > 0) store_tile(j - 1);
+    if (c == 0 && j > 0) ring_store<B>(g, part, tile_row0(j - 1), lane, wv);
     if (s + 1 < total) {
-      const uint32_t nxt = lds0 + ((s + 1) & 1u) * kRingStage;
+      const uint32_t nxt = lds0 + ((s + 1) & 1u) * Lay::kStage;
       uint32_t cn = c + 1;
       if (cn == nc) {
         cn = 0;
         src = ring_tile_src(g, tile_row0(j + 1), lane, wv);
       }
       ring_issue_weights(src, cn, nxt, wv);
-      ring_issue_acts(act, cn, nxt, wv);
+      ring_issue_acts<B>(act, cn, nxt, wv);
     }
-    ring_chunk<B>(smem, (s & 1u) * kRingStage, (s & 1u) * L.a_stage, L, acc);
+    ring_chunk<B>(smem, s & 1u, L, acc);
     if (++c == nc) {
-      // the 4 k-groups of a wave, then (in store_tile) the 4 waves, in a fixed order
+      // the 4 k-groups of a wave, then (in ring_store) the 4 waves, in a fixed order
 #pragma unroll
       for (int a = 0; a < B; ++a) {
         float v = acc[a];
         v += __shfl_xor(v, 16, 64);
         v += __shfl_xor(v, 32, 64);
-        if (lane < 16) part[(j & 1u) * 256u + (wv * 4 + a) * 16 + lane] = v;
+        if (lane < 16) part[(wv * ring_slots<B>() + a) * 16 + lane] = v;
         acc[a] = 0.0f;
       }
       c = 0;
@@ -745,7 +789,7 @@ __global__ __launch_bounds__(256) void gemv_ring_tiles_kernel(GemvArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));
   __syncthreads();
-  store_tile(j - 1);
+  ring_store<B>(g, part, tile_row0(j - 1), lane, wv);
 }
 
 // Several independent products in one launch (a descriptor list, e.g. the
@@ -970,18 +1014,22 @@ hipError_t launch_cfg(const Plan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The matrix-core kernel: one 16-row tile per workgroup (Q4_K, 2-4 rows,
-// k a multiple of 2048; select_gemv only picks it there).
+// The matrix-core kernels (Q4_K, 2-8 rows, k a multiple of 2048; select_gemv
+// only picks them there): one 16-row tile per workgroup, or the tile-walking
+// grid (k at least 4096: two chunks per tile).
 template <int TYPE, int B, bool SYNC>
 hipError_t launch_ring(const Plan& p, bool tiles_grid, hipStream_t s) {
-  if constexpr (TYPE == kQ4_K && B >= 2 && B <= 4) {
+  if constexpr (TYPE == kQ4_K && B >= 2 && B <= 8) {
+    typedef RingLayout<ring_slots<B>()> Lay;
     if (p.nb % 64 != 0) return hipErrorInvalidValue;
-    if (tiles_grid)
+    if (tiles_grid) {
+      if (p.nb < 128) return hipErrorInvalidValue;
       hipLaunchKernelGGL((gemv_ring_tiles_kernel<B, SYNC>), dim3(static_cast<uint32_t>(kRingGrid)), dim3(256),
-                         kRingTilesLds, s, make_args(p));
-    else
+                         Lay::kTilesLds, s, make_args(p));
+    } else {
       hipLaunchKernelGGL((gemv_ring_kernel<B, SYNC>), dim3(static_cast<uint32_t>((p.n + 15) / 16)), dim3(256),
-                         kRingLds, s, make_args(p));
+                         Lay::kLds, s, make_args(p));
+    }
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

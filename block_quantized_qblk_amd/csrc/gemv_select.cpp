@@ -25,15 +25,23 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
   v.sync = mode == kGemvInLaunch;
   v.fused = mode == kGemvLdsFused;
   const int64_t nb = k / 32;
-  // Q4_K at 2-4 activation rows with whole 2048-element chunks: the
+  // Q4_K at 2-8 activation rows with whole 2048-element chunks: the
   // matrix-core kernel with the direct-load LDS ring (gemv_ring_kernel).
   // Measured against the dot4 kernels with the in-launch quantization, it is
-  // faster on every 70B-, 7B- and shard-shaped matrix at 2, 3 and 4 rows
-  // (at 2 rows: 70B gate/up 44.7-47.1 against 49.5-49.9 us, down 24.9
-  // against 27.2, o 10.5 against 11.7, 7B down 11.4 against 16.0).
-  if (type == kQ4_K && b >= 2 && b <= 4 && k % 2048 == 0) {
+  // faster on every 70B-, 7B- and shard-shaped matrix at 2 to 8 rows (at 2
+  // rows: 70B gate/up 44.7-47.1 against 49.5-49.9 us, down 24.9 against 27.2,
+  // o 10.5 against 11.7, 7B down 11.4 against 16.0; at 8 rows: gate/up 69-72
+  // against 92-94 us, down 34 against 48, q/k/v 19.5 against 28.0).
+  // With more 16-row tiles than the two-per-CU grid holds and at least two
+  // chunks per tile, a fixed grid walks them (gemv_ring_tiles_kernel), so
+  // that each tile's first chunk loads while the last one's is computed: 70B
+  // gate/up with the in-launch quantization 50-52 against 56 us at 4 rows, 48
+  // against 55 at 3, q/k/v (640 tiles) 14.9 against 15.4 us; at 512 tiles or
+  // fewer (70B o and down) the one-tile kernel stays faster (o 10.9 against
+  // 11.3 us).
+  if (type == kQ4_K && b >= 2 && b <= 8 && k % 2048 == 0) {
     v.ring = true;
-    v.ring_tiles = (n + 15) / 16 > kRingGrid;
+    v.ring_tiles = (n + 15) / 16 > kRingGrid && k >= 4096;
     return v;
   }
   if (mode == kGemvLdsFused) {

@@ -110,11 +110,11 @@ struct GemvVariant {
   bool alds;  // activation rows staged in LDS
   bool fused; // activation quantized in every workgroup's LDS
   int waves;  // waves per workgroup (classic kernel)
-  bool ring;  // gemv_ring_kernel (Q4_K, 2-4 rows: matrix cores, direct-load LDS ring)
+  bool ring;  // gemv_ring_kernel (Q4_K, 2-8 rows: matrix cores, direct-load LDS ring)
   bool ring_tiles;  // ... as gemv_ring_tiles_kernel, a fixed grid walking the 16-row tiles
 };
 // The tile-walking grid of the matrix-core GEMV (two workgroups per CU); used
-// when the 16-row tiles outnumber it.
+// when the 16-row tiles outnumber it and a tile has at least two chunks.
 constexpr int64_t kRingGrid = 512;
 GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode);
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len);

@@ -195,7 +195,7 @@ qblk_status qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void
  * The descriptors are read on the host during the call (the array need not
  * outlive it); their outputs must not overlap. Results are bit-identical to
  * qblk_gemv on each descriptor, except where qblk_gemv runs the matrix-core
- * kernel (Q4_K with 2 to 4 activation rows and k a multiple of 2048;
+ * kernel (Q4_K with 2 to 8 activation rows and k a multiple of 2048;
  * qblk_gemv_variant names it gemv_ring_kernel or gemv_ring_tiles_kernel): there the same block
  * products and scale steps are summed in another fp32 order. Descriptors
  * with n == 0 are skipped.
@@ -291,9 +291,9 @@ qblk_status qblk_gemv_f32_noalloc(int type, const void *wq, int64_t n, int64_t k
  * kernel's template arguments: "gemv_kernel<type, rows, rows per wave,
  * chunks per step, in-launch quantization, activations in LDS, waves per
  * workgroup>", "gemv_ring_kernel<rows, in-launch quantization>" (Q4_K with 2
- * to 4 rows and k a multiple of 2048: matrix cores; one 16-row tile per
+ * to 8 rows and k a multiple of 2048: matrix cores; one 16-row tile per
  * workgroup), "gemv_ring_tiles_kernel<rows, in-launch quantization>" (the
- * same with more than 512 tiles: a fixed grid walks them) or
+ * same with more than 512 tiles and k >= 4096: a fixed grid walks them) or
  * "gemv_pipe_kernel<type, rows, rows per wave, per-workgroup quantization,
  * in-launch quantization, activations in LDS>". Written NUL-terminated into
  * name[len]. Lets a test check that the instances a workload runs are the

@@ -11,15 +11,18 @@ GEMV_RANDOM = [(37, 1024, 1), (300, 4096, 1), (129, 2304, 4), (64, 256, 8), (70,
                (3100, 512, 2), (16400, 512, 5),
                # a single row and two rows: one wave, most lanes past the last row
                (1, 256, 1), (2, 512, 3),
-               # Q4_K's matrix-core kernel (2-4 rows, k a multiple of 2048): one
+               # Q4_K's matrix-core kernel (2-8 rows, k a multiple of 2048): one
                # 2048-element chunk with a ragged last tile, and fewer rows than a tile
                (1000, 2048, 3), (5, 4096, 4)]
 
 # Q4_K's matrix-core kernel with exact fp32 arithmetic: (n, k, batch)
-GEMV_RING_EXACT = [(67, 4096, 2), (67, 4096, 3), (67, 4096, 4), (16, 2048, 4), (8208, 2048, 2),
-                   # more than 512 tiles (the tile-walking grid): a ragged last tile, and
-                   # 1025 tiles, so that one workgroup takes three and the others two
-                   (8200, 2048, 3), (16400, 2048, 4)]
+GEMV_RING_EXACT = [(67, 4096, 2), (67, 4096, 3), (67, 4096, 4), (16, 2048, 4), (67, 4096, 5), (16, 2048, 8),
+                   # more than 512 tiles of one chunk (the one-tile kernel)
+                   (8208, 2048, 2),
+                   # more than 512 tiles of two chunks or more (the tile-walking grid): a
+                   # ragged last tile, and 1025 tiles, so that one workgroup takes three and
+                   # the others two, at 3, 4, 6 and 8 rows
+                   (8200, 4096, 3), (16400, 4096, 4), (8200, 4096, 6), (16400, 4096, 8)]
 
 # qblk_gemv with exact fp32 arithmetic, every type: batch (n = 67, k = 2304 / 2336)
 GEMV_EXACT_BATCH = [1, 3, 8, 11]
@@ -51,14 +54,16 @@ GEMV_F32 = [(37, 1024, 1), (300, 4096, 3), (4100, 2304, 1), (9000, 8192, 1), (12
 GEMV_F32_IN_LAUNCH = [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1), (4096, 14336, 1),
                       (4096, 4096, 1), (1024, 4096, 2), (9000, 4096, 4), (16400, 2304, 3),
                       (3, 1 << 24, 1), (3, 1 << 24, 4),
-                      # the row-group classes of the 70B-shaped decode at k = 8192:
-                      # 8 rows per wave with the activations in LDS (gate/up at
-                      # batch 4), 4 rows per wave (q/k/v and o at batch 4), and
+                      # the row-group classes of the 70B-shaped decode at k = 8192
+                      # (Q4_K: the matrix-core kernels; the other types: 8 rows per
+                      # wave with the activations in LDS and 4 rows per wave), and
                       # their batch-1 controls
                       (16400, 8192, 4), (9000, 8192, 4), (16400, 8192, 1),
-                      # Q4_K's 8-wave workgroups (6k-8k rows of 8k weights, batch
-                      # 2-8), with a ragged last workgroup at 6200 rows
-                      (6200, 8192, 2), (8192, 8192, 8)]
+                      # the same at 2 and 8 rows, with a ragged last workgroup at 6200 rows
+                      (6200, 8192, 2), (8192, 8192, 8),
+                      # Q4_K's 8-wave dot4 workgroups (6k-8k rows, k above 4096 but not a
+                      # multiple of 2048, batch 2-8)
+                      (6200, 6400, 2), (8192, 6400, 8)]
 
 # qblk_gemv_f32 at the 70B-shaped decode's own matrices (q/k/v and gate/up
 # concatenated by rows), Q4_K, sampled rows: (name, n, k) x batch

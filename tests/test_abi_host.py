@@ -234,19 +234,22 @@ def test_gemv_multi_validation():
 def test_gemv_variant_names():
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 1, True) == \
         "gemv_kernel<3, 1, 4, 1, true, true, 4>"
-    # Q4_K at 2-4 activation rows with k a multiple of 2048: the matrix-core kernel
+    # Q4_K at 2-8 activation rows with k a multiple of 2048: the matrix-core kernel
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 4, True) == "gemv_ring_tiles_kernel<4, true>"
-    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8208, 2048, 3, False) == "gemv_ring_tiles_kernel<3, false>"
-    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 2048, 3, False) == "gemv_ring_kernel<3, false>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8208, 4096, 3, False) == "gemv_ring_tiles_kernel<3, false>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8208, 2048, 3, False) == "gemv_ring_kernel<3, false>"  # one chunk
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 4096, 3, False) == "gemv_ring_kernel<3, false>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 8, True) == "gemv_ring_tiles_kernel<8, true>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 8192, 3, False) == "gemv_ring_kernel<3, false>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 2304, 4, True) == "gemv_kernel<3, 4, 2, 1, true, true, 4>"
-    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 8192, 8, True) == "gemv_kernel<3, 8, 8, 1, true, false, 4>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 57344, 6400, 8, True) == "gemv_kernel<3, 8, 8, 1, true, false, 4>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q8_0, 8192, 8192, 4, True) == "gemv_kernel<2, 4, 4, 1, true, true, 4>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 1024, 2048, 1, True).startswith("gemv_pipe_kernel<3, 1, 2, true")
     assert qblk.qblk_gemv_variant(o.TYPE_Q8_0, 14336, 4096, 1, False) == \
         "gemv_kernel<2, 1, 2, 2, false, true, 4>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 8192, 2, True) == "gemv_ring_kernel<2, true>"
-    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 8192, 5, True) == \
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 8192, 5, True) == "gemv_ring_kernel<5, true>"
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 6400, 5, True) == \
         "gemv_kernel<3, 5, 4, 1, true, false, 8>"
     assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, 8192, 2304, 2, True) == \
         "gemv_kernel<3, 2, 2, 1, true, true, 4>"

@@ -194,7 +194,7 @@ def test_gemv_exact_arithmetic(wtype, batch):
 
 @pytest.mark.parametrize("n,k,batch", cases.GEMV_RING_EXACT)
 def test_gemv_ring_exact_arithmetic(n, k, batch):
-    """Q4_K's matrix-core GEMV (2-4 activation rows, k a multiple of 2048)
+    """Q4_K's matrix-core GEMV (2-8 activation rows, k a multiple of 2048)
     with power-of-two scales: every partial sum is exact in fp32, so y must
     equal the oracle bit for bit whatever the summation order."""
     print(f"gemv ring exact n={n} k={k} batch={batch}", flush=True)
