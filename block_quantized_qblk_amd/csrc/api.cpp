@@ -247,6 +247,10 @@ QBLK_EXPORT qblk_status qblk_gemm(int type, const void* wq, int64_t n, int64_t k
   if (wgs > kMaxGridThreads / 256 || (m + 127) / 128 > 65535 || k > kMaxGemmK)
     return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();
+  if (qblk::gemm_runs_gemv(type, n, k, m)) {  // few rows: the decode GEMV kernels
+    if (n > kMaxGridThreads / 64) return QBLK_ERR_UNSUPPORTED;
+    return finish(qblk::launch_gemv(type, wq, n, k, xq, m, y, ldy, stream));
+  }
   return finish(qblk::launch_gemm(type, wq, n, k, xq, m, y, ldy, stream));
 }
 

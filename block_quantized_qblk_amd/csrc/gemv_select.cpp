@@ -97,6 +97,20 @@ GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode) {
   return set(1, 1);
 }
 
+// qblk_gemm with at most 8 activation rows: the decode GEMV kernels stream
+// the weights faster than the few-rows GEMM, whose grid has one workgroup
+// per 64 weight rows. Measured (quantized activation, GEMM against GEMV):
+// at 1-4 rows on every type and shape (Q4_K 4096 x 14336 at 1 row 30.6
+// against 9.6 us, Q8_0 14336 x 4096 at 4 rows 20.1 against 18.7 us); at 8
+// rows with up to 8192 weight rows (Q4_0 4096 x 4096 14.1 against 7.7 us)
+// and wherever the matrix-core GEMV runs (Q4_K 14336 x 4096 13.5 against
+// 12.9 us), but not for Q4_0 / Q8_0 with 14336 rows (Q8_0 20.8 against 24.0).
+bool gemm_runs_gemv(int type, int64_t n, int64_t k, int64_t m) {
+  if (m > 8) return false;
+  if (m <= 4 || n <= 8192) return true;
+  return select_gemv(type, n, k, static_cast<int>(m), kGemvQuantized).ring;
+}
+
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len) {
   const char* t = v.sync ? "true" : "false";
   const char* a = v.alds ? "true" : "false";

@@ -117,6 +117,8 @@ struct GemvVariant {
 // when the 16-row tiles outnumber it and a tile has at least two chunks.
 constexpr int64_t kRingGrid = 512;
 GemvVariant select_gemv(int type, int64_t n, int64_t k, int b, int mode);
+// Whether qblk_gemm runs the decode GEMV kernels (at most 8 activation rows)
+bool gemm_runs_gemv(int type, int64_t n, int64_t k, int64_t m);
 int gemv_variant_name(const GemvVariant& v, char* buf, size_t len);
 // Where the in-launch handoff keeps its data: the activation buffer
 // (qblk_quantize_act layout, batch rows of k), the 8 flag copies of

@@ -330,7 +330,9 @@ qblk_status qblk_gemv_float(int type, const void *wq, int64_t n, int64_t k, cons
  * Per block the same integer dot and outside scales as qblk_gemv
  * ("llama.cpp 推理引擎", §6.4; wmrh.cn "bare engine" article, §2.2); prefill
  * processes many tokens at once and is compute-bound ("llama.cpp 推理引擎",
- * §7.3), hence the matrix cores.
+ * §7.3), hence the matrix cores. With at most 8 rows the call runs
+ * qblk_gemv's kernels where they are faster (m <= 4, n <= 8192, or Q4_K
+ * with k a multiple of 2048): results are then qblk_gemv's, bit for bit.
  * Errors as qblk_gemv (no batch limit), plus QBLK_ERR_UNSUPPORTED for
  * k > 2^24.
  */

@@ -232,7 +232,10 @@ def test_gemv_random(wtype, n, k, batch):
                                    (130, 257, 512), (256, 128, 4096), (16, 513, 2304),
                                    (33, 100, 256), (64, 1000, 4096), (17, 47, 7168),
                                    # one output, and rows long enough for many K steps
-                                   (1, 1, 256), (70, 65, 32768)])
+                                   (1, 1, 256), (70, 65, 32768),
+                                   # 5-8 rows past 8192 weight rows: the few-rows kernel
+                                   # for Q4_0 / Q8_0 (qblk_gemv's kernels at fewer rows)
+                                   (8, 9000, 1024)])
 def test_gemm_random(wtype, m, n, k):
     print(f"gemm {TNAME[wtype]} m={m} n={n} k={k}", flush=True)
     rng = np.random.default_rng(41 * wtype + m + n)
@@ -258,6 +261,23 @@ def test_gemv_ldy_and_empty_calls():
     qblk.qblk_gemv(o.TYPE_Q4_K, wq, 0, k, xq, b, y=ybig[:, :0])
     qblk.qblk_gemm(o.TYPE_Q4_K, wq, 0, k, xq, b, y=ybig[:, :0])
     assert np.all(host(ybig)[:, n:] == -7.0)
+
+
+def test_gemm_few_rows_runs_gemv_kernels():
+    """qblk_gemm with at most 8 rows runs qblk_gemv's kernels where they are
+    faster: its result is then qblk_gemv's bit for bit (and the few-rows
+    kernel's, on the remaining shapes, within the tolerance of the oracle)."""
+    print("gemm few rows", flush=True)
+    rng = np.random.default_rng(91)
+    for wtype, n, k, m in ((o.TYPE_Q4_K, 300, 4096, 1), (o.TYPE_Q4_K, 9000, 4096, 8),
+                           (o.TYPE_Q8_0, 700, 1024, 6), (o.TYPE_Q4_0, 9000, 512, 3)):
+        w = _special_rows(rng, n, k)
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        wq, xq = dev_pack(wtype, w), dev_quantize(x)
+        yg = host(qblk.qblk_gemm(wtype, wq, n, k, xq, m))
+        yv = host(qblk.qblk_gemv(wtype, wq, n, k, xq, m))
+        assert np.array_equal(yg.view(np.uint32), yv.view(np.uint32)), (wtype, n, k, m)
+        check_rel(yg, expected(wtype, w, x))
 
 
 @pytest.mark.parametrize("fn", ["gemv", "gemm"])
