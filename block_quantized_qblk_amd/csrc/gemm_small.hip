@@ -4,8 +4,9 @@
 // idle and most of each tile empty, while the product is still a stream of
 // the whole weight matrix. This form keeps every weight byte read once and
 // spreads the work over many small workgroups instead:
-//   * a workgroup owns 16 * NT = 64 weight rows (columns n of Y) and all m
-//     rows of X, padded to 16 * MT;
+//   * a workgroup owns 16 * NT weight rows (columns n of Y: 64, or 32 and
+//     16 for short matrices, so the grid fills the chip) and all m rows of X,
+//     padded to 16 * MT;
 //   * its four waves split the reduction over k into four contiguous,
 //     super-block-aligned quarters and add their partial tiles in LDS at the
 //     end, in a fixed order (the result does not depend on scheduling);
@@ -430,16 +431,27 @@ void launch_t(const WeightView& W, int64_t n, int64_t nb, const ActView& A, int6
                      ldy);
 }
 
+template <int TYPE, int NT>
+void launch_nt(const WeightView& W, int64_t n, int64_t nb, const ActView& A, int64_t m, float* y,
+               int64_t ldy, hipStream_t s) {
+  if (m <= 16) launch_t<TYPE, 1, NT, kWaves>(W, n, nb, A, m, y, ldy, s);
+  else if (m <= 32) launch_t<TYPE, 2, NT, kWaves>(W, n, nb, A, m, y, ldy, s);
+  else launch_t<TYPE, 4, NT, kWaves>(W, n, nb, A, m, y, ldy, s);
+}
+
+// Weight rows per workgroup (16 NT): each workgroup re-reads all m activation
+// rows, so wide tiles save that traffic (Q4_K 14336 x 4096, m = 64: 31.7 us
+// with 64 rows, 38.3 with 32, 57.7 with 16), but a short matrix then leaves
+// CUs idle, so the tile narrows until the grid holds about 256 workgroups
+// (Q4_K at m = 64 with 64 / 32 / 16 rows: 4096 x 14336 81.8 / 55.1 / 47.8
+// us, 8192 x 8192 51.4 / 35.8 / 55.1, 6144 x 4096 30.5 / 21.2 / 30.7,
+// 10240 x 4096 31.0 / 38.0 / 44.2). The results do not depend on it.
 template <int TYPE>
 void launch_type(const WeightView& W, int64_t n, int64_t nb, const ActView& A, int64_t m, float* y,
                  int64_t ldy, hipStream_t s) {
-  if (m <= 16) launch_t<TYPE, 1, 4, kWaves>(W, n, nb, A, m, y, ldy, s);
-  else if (m <= 32) launch_t<TYPE, 2, 4, kWaves>(W, n, nb, A, m, y, ldy, s);
-  // 64 weight rows per workgroup at every m: each workgroup re-reads all m
-  // activation rows, so the wider tile halves that traffic, which outweighs
-  // its register cost (one wave per SIMD) above 32 rows (Q4_K 14336 x 4096,
-  // m = 64: 32.7 against 38.9 us with 32 weight rows)
-  else launch_t<TYPE, 4, 4, kWaves>(W, n, nb, A, m, y, ldy, s);
+  if (n > 8192) launch_nt<TYPE, 4>(W, n, nb, A, m, y, ldy, s);
+  else if (n > 4096) launch_nt<TYPE, 2>(W, n, nb, A, m, y, ldy, s);
+  else launch_nt<TYPE, 1>(W, n, nb, A, m, y, ldy, s);
 }
 
 }  // namespace

@@ -235,7 +235,9 @@ def test_gemv_random(wtype, n, k, batch):
                                    (1, 1, 256), (70, 65, 32768),
                                    # 5-8 rows past 8192 weight rows: the few-rows kernel
                                    # for Q4_0 / Q8_0 (qblk_gemv's kernels at fewer rows)
-                                   (8, 9000, 1024)])
+                                   (8, 9000, 1024),
+                                   # the few-rows kernel's 32- and 16-row tiles (short matrices)
+                                   (40, 5000, 2304), (24, 4100, 1024)])
 def test_gemm_random(wtype, m, n, k):
     print(f"gemm {TNAME[wtype]} m={m} n={n} k={k}", flush=True)
     rng = np.random.default_rng(41 * wtype + m + n)
