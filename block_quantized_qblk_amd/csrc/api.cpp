@@ -241,9 +241,11 @@ QBLK_EXPORT qblk_status qblk_gemm(int type, const void* wq, int64_t n, int64_t k
   const qblk_status st = check_product(type, wq, n, k, xq, m, y, ldy);
   if (st != QBLK_OK || n == 0 || m == 0) return st;
   // grid: x = n / 128 workgroups of 256 work-items, y = m / 128 (<= 65535),
-  // or, for m <= 64, x = n / 64; a workgroup addresses its activation and
-  // weight rows with 32-bit offsets, so k is limited to 2^24
-  const int64_t wgs = m <= qblk::kGemmSmallMaxRows ? (n + 63) / 64 : (n + 127) / 128;
+  // or, in the few-rows form, x = n / 16 at most and y = m / 64; a workgroup
+  // addresses its activation and weight rows with 32-bit offsets, so k is
+  // limited to 2^24
+  const bool few = qblk::gemm_few_rows(n, m);
+  const int64_t wgs = few ? (n + 15) / 16 : (n + 127) / 128;
   if (wgs > kMaxGridThreads / 256 || (m + 127) / 128 > 65535 || k > kMaxGemmK)
     return QBLK_ERR_UNSUPPORTED;
   (void)hipGetLastError();

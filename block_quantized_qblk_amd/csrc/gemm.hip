@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n,
 
 hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq, int64_t m,
                        float* y, int64_t ldy, hipStream_t s) {
-  if (m <= kGemmSmallMaxRows) return launch_gemm_small(type, wq, n, k, xq, m, y, ldy, s);
+  if (gemm_few_rows(n, m)) return launch_gemm_small(type, wq, n, k, xq, m, y, ldy, s);
   WeightView W;
   W.base = static_cast<const uint8_t*>(wq);
   W.row_bytes = row_bytes(type, k);

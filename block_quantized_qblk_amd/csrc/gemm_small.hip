@@ -337,6 +337,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(WeightView W, in
                                                                 int64_t m, float* __restrict__ y, int64_t ldy) {
   static_assert(MT <= 4 && NT <= 4, "operand offsets are sized for 4 x 4 tiles");
   __shared__ __attribute__((aligned(16))) Shared<MT, NT, WAVES> sh;
+  // blockIdx.y: this workgroup's 16 MT activation rows (more than 64 rows)
+  {
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
+    A.q += m0 * A.k;
+    A.ds += m0 * nb * 8;
+    y += m0 * ldy;
+    m = m - m0 < 16 * MT ? m - m0 : 16 * MT;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -426,7 +434,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(WeightView W, in
 template <int TYPE, int MT, int NT, int WAVES>
 void launch_t(const WeightView& W, int64_t n, int64_t nb, const ActView& A, int64_t m, float* y, int64_t ldy,
               hipStream_t s) {
-  const dim3 grid(static_cast<uint32_t>((n + 16 * NT - 1) / (16 * NT)));
+  const dim3 grid(static_cast<uint32_t>((n + 16 * NT - 1) / (16 * NT)),
+                  static_cast<uint32_t>((m + 16 * MT - 1) / (16 * MT)));
   hipLaunchKernelGGL((gemm_small_kernel<TYPE, MT, NT, WAVES>), grid, dim3(64 * WAVES), 0, s, W, n, nb, A, m, y,
                      ldy);
 }

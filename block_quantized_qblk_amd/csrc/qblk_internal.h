@@ -167,8 +167,18 @@ hipError_t launch_gemv_float(int type, const void* wq, int64_t n, int64_t k, con
                              int64_t ldx, int64_t batch, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                        int64_t m, float* y, int64_t ldy, hipStream_t s);
-// rows at or below which launch_gemm takes the few-rows form
+// rows at or below which launch_gemm always takes the few-rows form
 constexpr int64_t kGemmSmallMaxRows = 64;
+// Whether launch_gemm takes the few-rows form (in 64-row chunks above 64
+// rows). The 128 x 128 kernel's time is about one workgroup's while its grid
+// holds at most one workgroup per CU, so on short matrices a few hundred rows
+// run faster as chunks of the few-rows kernel. Measured (Q4_K, main against
+// few-rows kernel): 4096 x 4096 at m = 256 91.0 against 57.0 us, 8192 x 8192
+// at 256 176.9 against 119.9, 14336 x 4096 at 128 91.8 against 64.3 (at 256
+// 92.7 against 121.7), 28672 x 4096 at 96 93.6 against 119.7; Q8_0 alike.
+inline bool gemm_few_rows(int64_t n, int64_t m) {
+  return m <= kGemmSmallMaxRows || (n <= 8192 && m <= 256) || (n <= 16384 && m <= 128);
+}
 hipError_t launch_gemm_small(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                              int64_t m, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,

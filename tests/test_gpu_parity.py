@@ -205,7 +205,7 @@ def test_gemv_ring_exact_arithmetic(n, k, batch):
 
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("m", [1, 16, 37, 64, 130])
+@pytest.mark.parametrize("m", [1, 16, 37, 64, 130, 300])
 def test_gemm_exact_arithmetic(wtype, m):
     print(f"gemm exact {TNAME[wtype]} m={m}", flush=True)
     n, k = 150, 1024 if wtype == o.TYPE_Q4_K else 1056
@@ -237,7 +237,10 @@ def test_gemv_random(wtype, n, k, batch):
                                    # for Q4_0 / Q8_0 (qblk_gemv's kernels at fewer rows)
                                    (8, 9000, 1024),
                                    # the few-rows kernel's 32- and 16-row tiles (short matrices)
-                                   (40, 5000, 2304), (24, 4100, 1024)])
+                                   (40, 5000, 2304), (24, 4100, 1024),
+                                   # the 128 x 128 kernel past the few-rows range: more than 256
+                                   # rows (ragged), and more than 128 rows past 8192 weight rows
+                                   (520, 300, 1024), (200, 8300, 512)])
 def test_gemm_random(wtype, m, n, k):
     print(f"gemm {TNAME[wtype]} m={m} n={n} k={k}", flush=True)
     rng = np.random.default_rng(41 * wtype + m + n)
