@@ -457,6 +457,121 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(WeightView W, int64_t n,
     }
 }
 
+// K split over two groups of four waves (a grid of at most one workgroup per
+// CU would otherwise run one wave per SIMD): group 0 takes the first half of
+// the K steps, group 1 the second, each with its own two stages; then group
+// 1's partial tiles pass through LDS and group 0 adds them to its own (in
+// that order) and stores. Both groups run the same number of steps (the
+// shorter one idles through its last), so their barriers pair up.
+template <int TYPE>
+__device__ __forceinline__ void step_ks(const GemmCtx<TYPE>& g, const DmaLanes<TYPE>& dl, const ScaleLanes& sl,
+                                        const Stage<TYPE>* __restrict__ cur, Stage<TYPE>* __restrict__ nxt,
+                                        int64_t st, int64_t send, bool active, int ltid, int lwave, int wm0,
+                                        int wn0, int half, int l32, const v16i& cinit, Acc& acc) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into `cur` are done
+  __syncthreads();                // everyone's; the previous readers of `nxt` are done
+  if (!active) return;            // uniform over the group
+  const bool more = st + 1 < send;
+  ScaleRegs sc;
+  if (more) {
+    sc = load_scales<TYPE>(g, sl, st + 1, ltid);
+    issue_codes<TYPE>(g, dl, nxt, st + 1, lwave);
+  }
+  const int nblk = static_cast<int>(g.nb - st * KB < KB ? g.nb - st * KB : KB);
+  compute<TYPE>(cur, nblk, wm0, wn0, half, l32, cinit, acc);
+  if (more) {
+    asm volatile("" ::: "memory");
+    store_scales<TYPE>(nxt, sc, st + 1, ltid);
+  }
+}
+
+template <int TYPE>
+__global__ __launch_bounds__(2 * kThreads) void gemm_ksplit_kernel(WeightView W, int64_t n, int64_t nb,
+                                                                   ActView A, int64_t m,
+                                                                   float* __restrict__ y, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) Stage<TYPE> stg[2][2];  // [K half][buffer]
+  static_assert(sizeof(float) * kWaves * TM * TN * 16 * 64 <= 2 * sizeof(Stage<TYPE>),
+                "group 1's partial tiles fit group 0's two stages");
+
+  const int tid = threadIdx.x;
+  const int grp = __builtin_amdgcn_readfirstlane(tid / kThreads);  // K half
+  const int ltid = tid % kThreads;
+  const int lane = tid & 63;
+  const int lwave = __builtin_amdgcn_readfirstlane(ltid >> 6);
+  const int wm0 = (lwave / kWavesN) * (32 * TM);
+  const int wn0 = (lwave % kWavesN) * (32 * TN);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  GemmCtx<TYPE> g;
+  g.W = W;
+  g.A = A;
+  g.n = n;
+  g.nb = nb;
+  g.m = m;
+  g.m0 = static_cast<int64_t>(blockIdx.y) * BM;
+  g.n0 = static_cast<int64_t>(blockIdx.x) * BN;
+
+  Acc acc;
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.main[a][b][v] = 0.0f;
+  v16i cinit;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cinit[v] = TYPE == kQ4_K ? kMagicBits : 0;
+
+  const int64_t steps = (nb + KB - 1) / KB;  // the launcher guarantees at least 2
+  const int64_t hsteps = (steps + 1) / 2;
+  const int64_t sbeg = grp ? hsteps : 0, send = grp ? steps : hsteps;
+  const ScaleLanes sl = scale_lanes<TYPE>(g, ltid);
+  const DmaLanes<TYPE> dl = dma_lanes<TYPE>(g, lwave, lane);
+  store_scales<TYPE>(&stg[grp][0], load_scales<TYPE>(g, sl, sbeg, ltid), sbeg, ltid);
+  issue_codes<TYPE>(g, dl, &stg[grp][0], sbeg, lwave);
+
+  for (int64_t i = 0; i < hsteps; ++i) {
+    const int64_t st = sbeg + i;
+    const bool active = st < send;
+    if (i & 1)
+      step_ks<TYPE>(g, dl, sl, &stg[grp][1], &stg[grp][0], st, send, active, ltid, lwave, wm0, wn0, half, l32,
+                    cinit, acc);
+    else
+      step_ks<TYPE>(g, dl, sl, &stg[grp][0], &stg[grp][1], st, send, active, ltid, lwave, wm0, wn0, half, l32,
+                    cinit, acc);
+  }
+
+  // group 1's partial tiles to group 0, through group 0's stages
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&stg[0][0]);
+  if (grp == 1) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[(((lwave * TM + tm) * TN + tn) * 16 + v) * 64 + lane] = acc.main[tm][tn][v];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int64_t gn = g.n0 + wn0 + 32 * tn + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float val = acc.main[tm][tn][v] + red[(((lwave * TM + tm) * TN + tn) * 16 + v) * 64 + lane];
+          const int64_t gm = g.m0 + wm0 + 32 * tm + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (gn < n && gm < m) y[gm * ldy + gn] = val;
+        }
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const void* xq, int64_t m,
@@ -469,6 +584,15 @@ hipError_t launch_gemm(int type, const void* wq, int64_t n, int64_t k, const voi
   const ActView A = make_act(xq, m, k);
   const int64_t nb = k / 32;
   const dim3 grid(static_cast<uint32_t>((n + BN - 1) / BN), static_cast<uint32_t>((m + BM - 1) / BM));
+  if (gemm_split_k(n, k, m)) {
+    switch (type) {
+      case kQ4_0: hipLaunchKernelGGL(gemm_ksplit_kernel<kQ4_0>, grid, dim3(2 * kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
+      case kQ8_0: hipLaunchKernelGGL(gemm_ksplit_kernel<kQ8_0>, grid, dim3(2 * kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
+      case kQ4_0H: hipLaunchKernelGGL(gemm_ksplit_kernel<kQ4_0H>, grid, dim3(2 * kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
+      default: hipLaunchKernelGGL(gemm_ksplit_kernel<kQ4_K>, grid, dim3(2 * kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
+    }
+    return hipGetLastError();
+  }
   switch (type) {
     case kQ4_0: hipLaunchKernelGGL(gemm_kernel<kQ4_0>, grid, dim3(kThreads), 0, s, W, n, nb, A, m, y, ldy); break;
     case kQ8_0: hipLaunchKernelGGL(gemm_kernel<kQ8_0>, grid, dim3(kThreads), 0, s, W, n, nb, A, m, y, ldy); break;

@@ -179,6 +179,12 @@ constexpr int64_t kGemmSmallMaxRows = 64;
 inline bool gemm_few_rows(int64_t n, int64_t m) {
   return m <= kGemmSmallMaxRows || (n <= 8192 && m <= 256) || (n <= 16384 && m <= 128);
 }
+// Whether the 128 x 128 kernel splits K over two groups of four waves: when
+// its grid holds at most one workgroup per CU (256), and K has at least two
+// steps of 128.
+inline bool gemm_split_k(int64_t n, int64_t k, int64_t m) {
+  return ((n + 127) / 128) * ((m + 127) / 128) <= 256 && k >= 256;
+}
 hipError_t launch_gemm_small(int type, const void* wq, int64_t n, int64_t k, const void* xq,
                              int64_t m, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_block_sums(int type, const void* wq, int64_t n, int64_t k, const void* xq,

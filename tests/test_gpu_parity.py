@@ -238,9 +238,12 @@ def test_gemv_random(wtype, n, k, batch):
                                    (8, 9000, 1024),
                                    # the few-rows kernel's 32- and 16-row tiles (short matrices)
                                    (40, 5000, 2304), (24, 4100, 1024),
-                                   # the 128 x 128 kernel past the few-rows range: more than 256
-                                   # rows (ragged), and more than 128 rows past 8192 weight rows
-                                   (520, 300, 1024), (200, 8300, 512)])
+                                   # the 128 x 128 kernel past the few-rows range, with K split over
+                                   # two wave groups (at most 256 workgroups): more than 256 rows
+                                   # (ragged), more than 128 rows past 8192 weight rows, and the
+                                   # shortest K (two steps); then more than 256 workgroups
+                                   (520, 300, 1024), (200, 8300, 512), (300, 700, 256),
+                                   (300, 12000, 256)])
 def test_gemm_random(wtype, m, n, k):
     print(f"gemm {TNAME[wtype]} m={m} n={n} k={k}", flush=True)
     rng = np.random.default_rng(41 * wtype + m + n)
