@@ -657,15 +657,15 @@ __device__ __forceinline__ void ring_store(const GemvArgs& g, const float* part,
   }
 }
 
-// One 16-row tile per workgroup (grid = tiles).
+// One 16-row tile (rows 16 tile ...) of the product g.
 template <int B, bool SYNC>
-__global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
+__device__ __forceinline__ void ring_one_tile(const GemvArgs& g, int64_t tile) {
   static_assert(B >= 1 && B <= 8, "up to 8 activation rows");
   typedef RingLayout<ring_slots<B>()> Lay;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t row0 = tile * 16;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
   const uint32_t nc = g.nb >> 6;  // the launcher guarantees nb % 64 == 0
   uint64_t tag = 0;
@@ -714,6 +714,12 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
   __builtin_amdgcn_s_waitcnt(ring_wait_imm(0));
   __syncthreads();
   ring_store<B>(g, part, row0, lane, wv);
+}
+
+// One 16-row tile per workgroup (grid = tiles).
+template <int B, bool SYNC>
+__global__ __launch_bounds__(256) void gemv_ring_kernel(GemvArgs g) {
+  ring_one_tile<B, SYNC>(g, blockIdx.x);
 }
 
 // A fixed grid walking the tiles: workgroup w takes tiles w, w + gridDim.x, ...,
@@ -801,6 +807,21 @@ struct GemvMulti {
   uint32_t first[kGemvMultiMax + 1];
   int count;
 };
+
+// The matrix-core form of the descriptor list (Q4_K, 2-8 rows, every k a
+// multiple of 2048): workgroups [first[i], first[i+1]) take the 16-row tiles
+// of descriptor i, each computed as the one-tile kernel computes it, so each
+// output is qblk_gemv's bit for bit.
+template <int B>
+__global__ __launch_bounds__(256) void gemv_ring_multi_kernel(GemvMulti m) {
+  const uint32_t block = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int t = 1; t < kGemvMultiMax; ++t)
+    if (t < m.count && block >= m.first[t]) i = t;  // uniform
+  ring_one_tile<B, false>(m.d[i], block - m.first[i]);
+}
+
 
 template <int TYPE, int B, int R, int U, bool ALDS>
 __global__ __launch_bounds__(256) void gemv_multi_kernel(GemvMulti m) {
@@ -1162,6 +1183,25 @@ hipError_t launch_multi_type(int b, GemvMulti& m, const int64_t* rows, int count
 
 }  // namespace
 
+template <int B>
+hipError_t launch_ring_multi_b(const GemvMulti& m, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_ring_multi_kernel<B>), dim3(m.first[m.count]), dim3(256),
+                     RingLayout<ring_slots<B>()>::kLds, s, m);
+  return hipGetLastError();
+}
+hipError_t launch_ring_multi(int b, const GemvMulti& m, hipStream_t s) {
+  switch (b) {
+    case 2: return launch_ring_multi_b<2>(m, s);
+    case 3: return launch_ring_multi_b<3>(m, s);
+    case 4: return launch_ring_multi_b<4>(m, s);
+    case 5: return launch_ring_multi_b<5>(m, s);
+    case 6: return launch_ring_multi_b<6>(m, s);
+    case 7: return launch_ring_multi_b<7>(m, s);
+    case 8: return launch_ring_multi_b<8>(m, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemv_multi(int type, const GemvDesc* d, int count, int64_t batch, hipStream_t s) {
   for (int64_t b0 = 0; b0 < batch; b0 += 8) {
     const int bc = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
@@ -1190,6 +1230,16 @@ hipError_t launch_gemv_multi(int type, const GemvDesc* d, int count, int64_t bat
     }
     if (used == 0) return hipSuccess;
     hipError_t e;
+    bool ring = type == kQ4_K && bc >= 2;
+    for (int i = 0; i < used; ++i) ring = ring && m.d[i].nb % 64 == 0;
+    if (ring) {
+      m.count = used;
+      m.first[0] = 0;
+      for (int i = 0; i < used; ++i) m.first[i + 1] = m.first[i] + static_cast<uint32_t>((rows[i] + 15) / 16);
+      e = launch_ring_multi(bc, m, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
     switch (type) {
       case kQ4_0: e = launch_multi_type<kQ4_0>(bc, m, rows, used, max_nb, s); break;
       case kQ8_0: e = launch_multi_type<kQ8_0>(bc, m, rows, used, max_nb, s); break;

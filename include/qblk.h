@@ -194,11 +194,12 @@ qblk_status qblk_gemv(int type, const void *wq, int64_t n, int64_t k, const void
  *   rows of k;  y : fp32 [batch][ldy].
  * The descriptors are read on the host during the call (the array need not
  * outlive it); their outputs must not overlap. Results are bit-identical to
- * qblk_gemv on each descriptor, except where qblk_gemv runs the matrix-core
- * kernel (Q4_K with 2 to 8 activation rows and k a multiple of 2048;
- * qblk_gemv_variant names it gemv_ring_kernel or gemv_ring_tiles_kernel): there the same block
- * products and scale steps are summed in another fp32 order. Descriptors
- * with n == 0 are skipped.
+ * qblk_gemv on each descriptor, with one exception: a Q4_K list at 2 to 8
+ * activation rows (per group of 8 rows) runs the matrix-core kernel only if
+ * every descriptor's k is a multiple of 2048; otherwise those whose k is
+ * (where qblk_gemv_variant names gemv_ring_kernel or gemv_ring_tiles_kernel)
+ * get the same block products and scale steps summed in another fp32 order.
+ * Descriptors with n == 0 are skipped.
  * Errors: QBLK_ERR_ARG (type, count < 0, null descs), the qblk_gemv errors of
  * any descriptor, QBLK_ERR_UNSUPPORTED (count > QBLK_GEMV_MULTI_MAX, batch >
  * QBLK_GEMV_MAX_BATCH).

@@ -647,12 +647,15 @@ def test_kv_scores_70b_shape_sampled(wtype, n_ctx, n_tok):
 
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("batch,ks", [(1, (4096, 4096, 2304)), (3, (1024, 1024, 2048)),
-                                      (1, (28672, 4096, 256)), (9, (512, 512, 768))])
+                                      (1, (28672, 4096, 256)), (9, (512, 512, 768)),
+                                      # every k a multiple of 2048: the matrix-core form
+                                      (4, (4096, 4096, 2048)), (10, (2048, 2048, 4096))])
 def test_gemv_multi_matches_single_products(wtype, batch, ks):
     """Three descriptors (q/k/v-like row counts, one with its own activation
     and k) in one launch: each output is bit-identical to its own qblk_gemv
-    (within 1e-6 where qblk_gemv runs the matrix-core kernel, which sums the
-    same terms in another order) and within the bar of the oracle."""
+    (within 1e-6 where qblk_gemv runs the matrix-core kernel but the list
+    mixes k that it cannot take, so the list runs the dot4 kernel) and within
+    the bar of the oracle."""
     print(f"gemv multi {TNAME[wtype]} batch={batch} ks={ks}", flush=True)
     rng = np.random.default_rng(160 + wtype + batch)
     ns = (300, 77, 1030)
@@ -669,9 +672,10 @@ def test_gemv_multi_matches_single_products(wtype, batch, ks):
         prods.append((wq, n, k, xq, y[:, :n]))
         refs.append((w, xs[k], qblk.qblk_gemv(wtype, wq, n, k, xq, batch), y))
     qblk.qblk_gemv_multi(wtype, prods, batch)
+    ring_list = wtype == o.TYPE_Q4_K and all(k % 2048 == 0 for (_, _, k, _, _) in prods)
     for (w, x, ysingle, ybig), (_, n, k, _, _) in zip(refs, prods):
         yh = host(ybig)
-        if qblk.qblk_gemv_variant(wtype, n, k, batch, False).startswith("gemv_ring"):
+        if not ring_list and qblk.qblk_gemv_variant(wtype, n, k, batch, False).startswith("gemv_ring"):
             # qblk_gemv runs the matrix-core kernel here: the same block
             # products and scale steps, summed in another order
             ys = host(ysingle)
