@@ -39,7 +39,7 @@ GEMV_FULL_SIZE = [
 
 # qblk_gemv, 70B-shaped Q4_K matrices, sampled rows: (name, n, k) x batch
 GEMV_70B = [("q", 8192, 8192), ("gate", 28672, 8192), ("down", 8192, 28672)]
-GEMV_70B_BATCH = [1, 4]
+GEMV_70B_BATCH = [1, 4, 8]
 
 # qblk_gemm at m rows of Q4_K 14336 x 4096; for m <= 64 qblk_gemv on the same inputs
 GEMM_PREFILL_M = [512, 1, 8, 64]
