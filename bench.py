@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--traffic-probe", action="store_true",
                    help="only run a 1 GiB device copy and the GEMVs of 4 layers once "
                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
+    p.add_argument("--batch4-probe", action="store_true",
+                   help="only run a 1 GiB device copy and one batch-4 decode token of 4 layers "
+                        "(the matrix-core GEMV kernels; for rocprofv3 --pmc runs)")
     return p.parse_args()
 
 
@@ -340,6 +343,9 @@ def main():
     if args.traffic_probe:
         traffic_probe(torch, qblk, synth, dev)
         return
+    if args.batch4_probe:
+        batch4_probe(torch, qblk, synth, dev)
+        return
 
     # ------------------------------------------------------------ 70B decode, batch 1 and 4
     t0 = time.time()
@@ -531,6 +537,27 @@ def traffic_probe(torch, qblk, synth, dev):
                       "gemm_launch": gemm,
                       "gemv_sources_sha256": sources_sha256(GEMV_SOURCES),
                       "gemm_sources_sha256": sources_sha256(GEMM_SOURCES)}))
+
+
+def batch4_probe(torch, qblk, synth, dev):
+    """For rocprofv3 --pmc runs: a 1 GiB device copy (calibration), then one
+    decode token of four 70B-shaped layers at batch 4 (per layer: qkv, o,
+    gate_up, down on the matrix-core kernels). Prints the algorithmic bytes
+    of every GEMV launch, in launch order."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    m = DecodeModel(torch, qblk, synth, synth.LAYER_70B, 4, 5000, "student_t", 4, dev)
+    m.token()
+    torch.cuda.synchronize()
+    gemv = [{"group": g, "n": n, "k": k, "kernel": qblk.qblk_gemv_variant(qblk.Q4_K, n, k, 4, True),
+             "alg_bytes": alg_bytes(qblk, n, k, 4, True)}
+            for _ in range(4) for g, _, n, k in m.groups]
+    print(json.dumps({"copy_bytes_each_way": 1 << 30, "gemv_launches": gemv,
+                      "gemv_sources_sha256": sources_sha256(GEMV_SOURCES)}))
 
 
 def gemv_launches(synth):
