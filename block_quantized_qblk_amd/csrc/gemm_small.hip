@@ -332,13 +332,15 @@ __device__ __forceinline__ void compute_group(Ops<TYPE, MT, NT> o, const ScaleTa
   }
 }
 
-template <int TYPE, int MT, int NT, int WAVES>
+template <int TYPE, int MT, int NT, int WAVES, bool CHUNKS>
 __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(WeightView W, int64_t n, int64_t nb, ActView A,
                                                                 int64_t m, float* __restrict__ y, int64_t ldy) {
   static_assert(MT <= 4 && NT <= 4, "operand offsets are sized for 4 x 4 tiles");
   __shared__ __attribute__((aligned(16))) Shared<MT, NT, WAVES> sh;
-  // blockIdx.y: this workgroup's 16 MT activation rows (more than 64 rows)
-  {
+  // CHUNKS (more than 64 rows): blockIdx.y picks this workgroup's 16 MT
+  // activation rows (a separate instance: the offsets cost the 64-row
+  // instance, at its register limit, 7% at 14336 x 4096)
+  if constexpr (CHUNKS) {
     const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
     A.q += m0 * A.k;
     A.ds += m0 * nb * 8;
@@ -436,8 +438,12 @@ void launch_t(const WeightView& W, int64_t n, int64_t nb, const ActView& A, int6
               hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>((n + 16 * NT - 1) / (16 * NT)),
                   static_cast<uint32_t>((m + 16 * MT - 1) / (16 * MT)));
-  hipLaunchKernelGGL((gemm_small_kernel<TYPE, MT, NT, WAVES>), grid, dim3(64 * WAVES), 0, s, W, n, nb, A, m, y,
-                     ldy);
+  if (m > 16 * MT)
+    hipLaunchKernelGGL((gemm_small_kernel<TYPE, MT, NT, WAVES, true>), grid, dim3(64 * WAVES), 0, s, W, n, nb, A, m,
+                       y, ldy);
+  else
+    hipLaunchKernelGGL((gemm_small_kernel<TYPE, MT, NT, WAVES, false>), grid, dim3(64 * WAVES), 0, s, W, n, nb, A,
+                       m, y, ldy);
 }
 
 template <int TYPE, int NT>
