@@ -19,9 +19,11 @@ _lib = None
 
 
 class QblkError(RuntimeError):
-    def __init__(self, status, what):
+    def __init__(self, status, what, hip_error=None):
         self.status = status
-        super().__init__(f"{what}: status {status} ({strerror(status)})")
+        self.hip_error = hip_error
+        extra = f", hipError_t {hip_error}" if hip_error is not None else ""
+        super().__init__(f"{what}: status {status} ({strerror(status)}{extra})")
 
 
 def _load():
@@ -32,6 +34,11 @@ def _load():
         # there is no fallback path: the library must have been built
         raise RuntimeError(f"{LIB_PATH} is missing; build it first with "
                            "`python -m block_quantized_qblk_amd.build_lib`")
+    # torch's HIP runtime libraries are loaded before the library's own
+    # (ROCm's): a process that had loaded ROCm's HIP and HSA libraries first
+    # and then initialised torch's saw the library's first launch fail with
+    # hipErrorNoDevice
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     sig = {
@@ -90,7 +97,9 @@ def _ptr(t):
 
 def _check(status, what):
     if status != 0:
-        raise QblkError(status, what)
+        # a failed launch: the HIP error code the library kept for it
+        hip = int(_load().qblk_last_hip_error()) if status == -5 else None  # QBLK_ERR_LAUNCH
+        raise QblkError(status, what, hip)
 
 
 def _require_cuda(t, name, rows=False):

@@ -65,6 +65,14 @@ GEMV_F32_IN_LAUNCH = [(9000, 8192, 1), (20000, 4096, 1), (8192, 28672, 1), (4096
                       # multiple of 2048, batch 2-8)
                       (6200, 6400, 2), (8192, 6400, 8)]
 
+# qblk_gemv_f32, Q4_K on the tile-walking matrix-core kernel with the
+# in-launch handoff: 513-750 tiles of 2-5 chunks (so that some workgroups of
+# the 512-workgroup grid take two tiles), every batch 2-8
+GEMV_F32_RING_TILES = [(8200, 4096, 2), (9000, 6144, 3), (8208, 8192, 4), (12000, 10240, 5),
+                  (8200, 4096, 6), (9000, 4096, 7), (10000, 8192, 8)]
+# ... and with exact fp32 arithmetic (power-of-two scales)
+GEMV_F32_RING_TILES_EXACT = [(8200, 4096, 3), (9000, 6144, 8)]
+
 # qblk_gemv_f32 at the 70B-shaped decode's own matrices (q/k/v and gate/up
 # concatenated by rows), Q4_K, sampled rows: (name, n, k) x batch
 GEMV_F32_70B = [("qkv", 10240, 8192), ("o", 8192, 8192), ("gate_up", 57344, 8192),
@@ -100,6 +108,9 @@ def covered():
     for m in GEMM_PREFILL_M:
         if m <= 64:
             out.add((Q4_K, 14336, 4096, m, False))
+    for n, k, b in GEMV_F32_RING_TILES + GEMV_F32_RING_TILES_EXACT:
+        out.add((Q4_K, n, k, b, True))
+        out.add((Q4_K, n, k, b, False))
     for _, n, k in GEMV_F32_70B:
         for b in GEMV_F32_70B_BATCH:
             out.add((Q4_K, n, k, b, True))

@@ -419,6 +419,41 @@ def test_gemv_f32_in_launch_quantization_reused_workspace(wtype, n, k, batch):
         check_rel(fused[:, rows], expected(wtype, w[rows], x))
 
 
+@pytest.mark.parametrize("n,k,batch", cases.GEMV_F32_RING_TILES)
+def test_gemv_f32_ring_tiles(n, k, batch):
+    """Q4_K's tile-walking matrix-core kernel with the in-launch handoff, on
+    grids where some workgroups take a second tile: bitwise equal to quantize
+    + qblk_gemv on two calls, no fallback, within the tolerance of the
+    oracle."""
+    t = torch()
+    print(f"gemv_f32 ring tiles n={n} k={k} batch={batch}", flush=True)
+    assert qblk.qblk_gemv_variant(o.TYPE_Q4_K, n, k, batch, True).startswith("gemv_ring_tiles_kernel")
+    rng = np.random.default_rng(n + 7 * k + batch)
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    wq = dev_pack(o.TYPE_Q4_K, w)
+    xd = dev(x)
+    work = t.zeros(qblk.qblk_gemv_f32_work_bytes(batch, k), dtype=t.uint8, device="cuda")
+    for call in range(2):
+        fused = host(qblk.qblk_gemv_f32(o.TYPE_Q4_K, wq, n, k, xd, work=work))
+        two_step = host(qblk.qblk_gemv(o.TYPE_Q4_K, wq, n, k, qblk.qblk_quantize_act(xd), batch))
+        assert np.array_equal(fused.view(np.uint32), two_step.view(np.uint32)), call
+    assert qblk.handoff_fallbacks(work, batch, k) == 0
+    rows = _sample_rows(n, 24, n + batch)
+    check_rel(fused[:, rows], expected(o.TYPE_Q4_K, w[rows], x))
+
+
+@pytest.mark.parametrize("n,k,batch", cases.GEMV_F32_RING_TILES_EXACT)
+def test_gemv_f32_ring_tiles_exact_arithmetic(n, k, batch):
+    """The tile-walking kernel with the in-launch handoff and power-of-two
+    scales: every partial sum is exact in fp32, so y equals the oracle bit
+    for bit."""
+    print(f"gemv_f32 ring tiles exact n={n} k={k} batch={batch}", flush=True)
+    packed, x, y32 = _exact_case(o.TYPE_Q4_K, n, k, batch, 990 + batch)
+    y = qblk.qblk_gemv_f32(o.TYPE_Q4_K, dev(packed.reshape(-1)), n, k, dev(x))
+    assert np.array_equal(host(y), y32)
+
+
 @pytest.mark.parametrize("batch", cases.GEMV_F32_70B_BATCH)
 @pytest.mark.parametrize("name,n,k", cases.GEMV_F32_70B)
 def test_gemv_f32_70b_decode_shapes_sampled(name, n, k, batch):
@@ -444,14 +479,15 @@ def test_gemv_f32_70b_decode_shapes_sampled(name, n, k, batch):
 
 @pytest.mark.parametrize("wtype", [o.TYPE_Q4_K, o.TYPE_Q8_0])
 @pytest.mark.parametrize("n,k,batch", [(9000, 8192, 1), (16400, 8192, 4), (16400, 2304, 3),
-                                       (3, 1 << 20, 4)])
+                                       (3, 1 << 20, 4), (8200, 4096, 2), (10000, 8192, 8)])
 def test_gemv_f32_handoff_fallback_is_bit_exact(wtype, n, k, batch):
     """With the handoff's wait bound set to 0 ticks every workgroup that
     finds a slice unpublished quantizes the whole activation itself, racing
     the producers over the same workspace bytes: the result is still bitwise
     that of quantize + qblk_gemv, and the workspace counter records the
     fallbacks. (3, 2^20, 4): one workgroup, which publishes every slice itself
-    before it waits."""
+    before it waits. Q4_K at (16400, 8192, 4), (8200, 4096, 2) and (10000,
+    8192, 8): the tile-walking matrix-core kernel."""
     if wtype == o.TYPE_Q4_K and k % 256:
         pytest.skip("Q4_K needs k % 256 == 0")
     t = torch()
